@@ -1,0 +1,67 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is the oracle's own source with one plausible error written into
+it (a dropped term, a wrong sign or index, a transposed operand, ...), loaded
+as a separate module on the CPU.  The real oracle is never modified.
+"""
+
+import os
+import types
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "attention.py")
+
+MUTANTS = {
+    "dropped_scale": ("scores = (qh @ kh.T) * scale", "scores = (qh @ kh.T)"),
+    "transposed_scores": ("scores = (qh @ kh.T) * scale", "scores = (kh @ qh.T) * scale"),
+    "causal_wrong_direction": ("ok = ok & (j <= i)", "ok = ok & (j >= i)"),
+    "causal_strict": ("ok = ok & (j <= i)", "ok = ok & (j < i)"),
+    "padding_off_by_one": ("    ok = j < key_len\n    if causal:", "    ok = j <= key_len\n    if causal:"),
+    "rows_padding_off_by_one": ("        ok = j < key_len\n", "        ok = j <= key_len\n"),
+    "gqa_interleaved": ("return (h * n_kv_heads) // n_q_heads", "return h % n_kv_heads"),
+    "no_max_subtraction": ("e = np.exp(scores - m[:, None])", "e = np.exp(scores)"),
+    "no_normalisation": ("p = e / safe[:, None]", "p = e"),
+    "lse_missing_max": ("lse = np.where(has_key, m + np.log(safe), -np.inf)",
+                        "lse = np.where(has_key, np.log(safe), -np.inf)"),
+    "lse_log2": ("lse = np.where(has_key, m + np.log(safe), -np.inf)",
+                 "lse = np.where(has_key, m + np.log2(safe), -np.inf)"),
+    "transposed_pv": ("out = p @ vh", "out = p.T @ vh"),
+    "default_scale_1_over_d": ("return 1.0 / math.sqrt(d)", "return 1.0 / d"),
+    "rows_dropped_scale": ("sc = (kh @ qi) * scale", "sc = (kh @ qi)"),
+    "rows_causal_strict": ("ok &= j <= i", "ok &= j < i"),
+    "rows_no_max": ("e = np.exp(sc - m)", "e = np.exp(sc)"),
+    "rows_masked_not_zeroed": ("            out[n] = 0.0\n            lse[n] = -np.inf\n            continue",
+                               "            lse[n] = -np.inf\n            out[n] = 1.0\n            continue"),
+    "rows_lse_missing_max": ("lse[n] = m + np.log(den)", "lse[n] = np.log(den)"),
+    "rows_gqa_wrong_head": ("kh = np.asarray(k[b, :, g, :], dtype=np.float64)",
+                            "kh = np.asarray(k[b, :, h % k.shape[2], :], dtype=np.float64)"),
+    "pad_key_len_ignores_batch": ("return int(min(max(int(pad_lens[b]), 0), s))",
+                                  "return int(min(max(int(pad_lens[0]), 0), s))"),
+}
+
+
+def _load_mutant(find, repl):
+    src = open(SRC).read()
+    assert src.count(find) == 1, f"mutation anchor not unique/found: {find!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(find, repl), "oracle_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    mod = _load_mutant(*MUTANTS[name])
+    caught = []
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        for pin in oracle_pins.ALL_PINS:
+            try:
+                pin(mod)
+            except (AssertionError, FloatingPointError, ValueError, IndexError) as e:
+                caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
