@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+A step is one attn_fwd call over one batch of seeded synthetic input of the
+Llama-2-7B-shaped causal prefill (B=1, H=32, S=2048, D=128, bf16) with inputs
+already resident in device memory.  Throughput counts 4·B·H·S²·D FLOPs,
+halved under causal masking, over the wall time of K timed steps; the
+roofline block divides the same FLOP count by the kernel's average duration
+measured with HIP events on the launch stream.  The cpu_baseline block times
+the fp64 CPU oracle on a bounded sample of heads of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--all]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused attention fwd TFLOP/s (bf16, causal) and % of MI355X MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "llama2_7b_prefill"
+
+
+def metric_flops(w):
+    f = 4.0 * w.B * w.Hq * w.S * w.S * w.D
+    return f / 2.0 if w.causal else f
+
+
+def min_hbm_bytes(w, pad):
+    """Q, K, V read once, O (and LSE) written once (the score matrix never
+    reaches memory)."""
+    el = {"bf16": 2, "fp16": 2, "fp32": 4}[w.dtype]
+    qo = 2 * w.B * w.S * w.Hq * w.D * el
+    kv = 2 * w.B * w.S * w.Hkv * w.D * el
+    lse = w.B * w.Hq * w.S * 4 if w.want_lse else 0
+    return qo + kv + lse
+
+
+def run_gpu(w, steps, warmup):
+    import torch
+    from transformer_attention_06_amd import attn as A
+    from transformer_attention_06_amd import workloads as W
+
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    q, k, v, pad = W.make_inputs(w)
+    qd = torch.from_numpy(q).to(dt).cuda()
+    kd = torch.from_numpy(k).to(dt).cuda()
+    vd = torch.from_numpy(v).to(dt).cuda()
+    del q, k, v
+    pad_d = None if pad is None else torch.from_numpy(pad).cuda()
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda") if w.want_lse else None
+    mask = A.ATTN_MASK_NONE if pad is None else A.ATTN_MASK_KEY_PADDING
+    stream = torch.cuda.current_stream()
+
+    def step():
+        A.attn_fwd(qd, kd, vd, mask, pad_d, None, w.causal, w.Hq, w.Hkv, out, lse, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # HIP events on the launch stream bracket every launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return dict(ms_per_step=(t1 - t0) * 1e3 / steps, kernel_ms_mean=float(kern_ms.mean()),
+                kernel_ms_median=float(np.median(kern_ms)), kernel_ms_min=float(kern_ms.min()),
+                pad=pad)
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """Time the fp64 oracle on whole (batch, head) units of the workload until
+    the time budget is spent; report the metric's unit (TFLOP/s)."""
+    import oracle
+    from transformer_attention_06_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    import torch
+    q, k, v, pad = W.make_inputs(w)
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    rnd = lambda x: torch.from_numpy(x).to(dt).to(torch.float32).numpy()
+    q, k, v = rnd(q), rnd(k), rnd(v)
+    scale = 1.0 / np.sqrt(w.D)
+    done = 0
+    t0 = time.perf_counter()
+    units = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    for (b, h) in units:
+        g = oracle.kv_head_for(h, w.Hq, w.Hkv)
+        kl = w.S if pad is None else int(pad[b])
+        oracle.attention_head(q[b, :, h, :], k[b, :, g, :], v[b, :, g, :], scale, w.causal, kl)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = metric_flops(w) * done / len(units)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(units)} (batch, head) units of {w.name}, fp64 numpy, "
+                      f"full SxS score matrix, {el:.2f} s wall"}
+
+
+def bench_one(name, steps, warmup, with_cpu):
+    from transformer_attention_06_amd import workloads as W
+    w = W.WORKLOADS[name]
+    r = run_gpu(w, steps, warmup)
+    fl = metric_flops(w)
+    value = fl / (r["ms_per_step"] * 1e-3) / 1e12
+    achieved = fl / (r["kernel_ms_mean"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape; no weights)",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "causal": w.causal, "mask": "key_padding" if w.mask_kind else "none",
+                   "lse": w.want_lse, "pct_of_peak_wall": round(100 * value / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 3),
+                     "kernel_us_median": round(r["kernel_ms_median"] * 1e3, 3),
+                     "flops_per_launch": fl,
+                     "min_hbm_bytes_per_launch": min_hbm_bytes(w, r["pad"])},
+    }
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(w)
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="one line per workload (no CPU leg)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X).", file=sys.stderr)
+        sys.exit(1)
+    if args.all:
+        from transformer_attention_06_amd import workloads as W
+        for name in W.WORKLOADS:
+            print(json.dumps(bench_one(name, args.steps, args.warmup, False)), flush=True)
+        return
+    print(json.dumps(bench_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline)),
+          flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,129 @@
+/*
+ * attn_fwd.h — C ABI of the MI355X (gfx950) fused attention forward library
+ * (libattn_fwd.so).
+ *
+ * The operation (one call = one fused kernel launch):
+ *
+ *   for every batch b and query head h, with kv head g = floor(h*Hkv/Hq):
+ *     S    = (Q[b,:,h,:] · K[b,:,g,:]ᵀ) · scale
+ *     S_ij = -inf where key j is masked (causal: j > i; key padding: j >= L_b)
+ *     P    = softmax(S) along keys;   O[b,:,h,:] = P · V[b,:,g,:]
+ *     LSE  = ln(sum_j exp(S_ij))      (natural log of the scaled scores)
+ *
+ * This is the chain "Q·Kᵀ → Scale → Mask → Softmax → Drop → ·V" that the page
+ * "CANN-ATB图优化-昇腾NPU怎么把PyTorch计算图改造成融合算子" (Pattern 2, SDPA →
+ * FlashAttention) replaces by one FlashAttention(Q, K, V, mask, scale) call,
+ * with dropout as the identity (inference forward).  The kernel computes it
+ * blockwise with an online softmax, as "ops-transformer：Transformer算子融合与
+ * 推理加速实战" §2.2 and §3.2 describe: the S×S score matrix never reaches
+ * device memory.  The call parameters (scale, mask type, whether to output the
+ * intermediate LSE) follow the same page's §4.2; the head counts and the
+ * causal flag follow the MhaV3 parameters of the ATB engineering guide
+ * (hwcomputing.csdn.net/6a59a88310ee7a33f28e5ce9) §8.2.
+ *
+ * Conventions
+ *   - Layout: every tensor is contiguous (B, S, H, D), row-major, D fastest
+ *     ("ops-transformer…" §2.3/§4.2).  q and out have H = n_q_heads; k and v
+ *     have H = n_kv_heads.  q, k, v share B, S and D (self-attention).
+ *   - Pointers are DEVICE pointers (HIP), except the descriptor structs
+ *     themselves, which are host memory read during the call only.
+ *   - Ownership: the caller allocates and owns every buffer.  The library
+ *     never allocates, frees or synchronises device memory and keeps no
+ *     state between calls; it is re-entrant and thread-safe.
+ *   - Asynchrony: the kernel is enqueued on `stream` (a hipStream_t; NULL =
+ *     the default stream).  ATTN_OK means "enqueued"; a device-side fault
+ *     surfaces at the caller's next synchronisation.
+ *   - Validation: every argument check runs on the host before any HIP call,
+ *     so an error return leaves the device untouched.  B == 0 or S == 0
+ *     returns ATTN_OK without a launch ("ops-transformer…" §6.4: empty input).
+ *   - Supported: dtype fp32, fp16, bf16 (q, k, v and out all the same);
+ *     D in {64, 128} (the page "CANN-ops-transformer和ATB-昇腾NPU上算子和加速库
+ *     怎么配合" gates its fused kernel on head_dim; other D return
+ *     ATTN_ERR_UNSUPPORTED: there is no fallback path).
+ *   - Precision: 16-bit inputs run both products on bf16/fp16 MFMA with fp32
+ *     accumulation; the running max, running sum and output accumulator are
+ *     fp32 and the output is rounded to the input dtype only at the end
+ *     ("ops-transformer…" §2.4).  The probabilities P are rounded to the input
+ *     dtype before the P·V product.  fp32 inputs keep everything in fp32.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_F32 = 0,
+    ATTN_F16 = 1,
+    ATTN_BF16 = 2
+} attn_dtype_t;
+
+typedef enum {
+    ATTN_MASK_NONE = 0,        /* no padding mask                              */
+    ATTN_MASK_KEY_PADDING = 1  /* batch b sees keys j < pad_lens[b] only       */
+} attn_mask_kind_t;
+
+/* Tensor descriptor: a contiguous (B, S, H, D) device buffer. */
+typedef struct {
+    void*   data;   /* device pointer, 16-byte aligned                        */
+    int32_t dtype;  /* attn_dtype_t                                            */
+    int64_t B, S, H, D;
+} attn_tensor_t;
+
+/* Return codes (0 = success, negative = error). */
+enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,        /* a required pointer is NULL                   */
+    ATTN_ERR_SHAPE = -2,       /* B/S/D disagree between tensors, or negative  */
+    ATTN_ERR_HEADS = -3,       /* head counts disagree or Hq % Hkv != 0        */
+    ATTN_ERR_DTYPE = -4,       /* unknown dtype or tensors of mixed dtype      */
+    ATTN_ERR_UNSUPPORTED = -5, /* D not in {64, 128}, or sizes beyond limits   */
+    ATTN_ERR_MASK = -6,        /* bad mask_kind / pad_lens / causal value      */
+    ATTN_ERR_ALIGN = -7,       /* a data pointer is not 16-byte aligned        */
+    ATTN_ERR_LAUNCH = -8,      /* the HIP launch failed                        */
+    ATTN_ERR_DEVICE = -9       /* the current device is not gfx950             */
+};
+
+/*
+ * attn_fwd — fused scaled-dot-product attention forward.
+ *
+ *   q, k, v     input descriptors (see above).  q: (B,S,Hq,D); k, v: (B,S,Hkv,D).
+ *   mask_kind   ATTN_MASK_NONE or ATTN_MASK_KEY_PADDING.
+ *   pad_lens    device int32[B] of valid key lengths when mask_kind is
+ *               ATTN_MASK_KEY_PADDING (must be NULL otherwise).  Values are
+ *               clamped to [0, S] on the device; a batch with length 0 has
+ *               no visible key.
+ *   scale       multiplier of Q·Kᵀ; any value that is not > 0 (0, negative,
+ *               NaN) selects the default 1/sqrt(D) ("ops-transformer…" §4.2).
+ *   causal      0 or 1; key j is visible to query i only if j <= i.  Causal
+ *               and key padding compose (both must allow a key).
+ *   n_q_heads   Hq (== q->H == out->H);  n_kv_heads  Hkv (== k->H == v->H),
+ *               Hq % Hkv == 0; query head h reads kv head floor(h*Hkv/Hq).
+ *   out         output descriptor: same B, S, D and dtype as q, H = Hq.
+ *               A row with no visible key is written as zeros.
+ *   lse         device float[B, Hq, S] receiving ln(sum_j exp(S_ij)) per row
+ *               (-inf for a row with no visible key), or NULL to skip it.
+ *   stream      hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Limits: S < 2^31 / 4, B*S*H*D < 2^62, Hq <= 65535.
+ * Returns ATTN_OK or one of the negative codes above.
+ */
+int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+             int mask_kind, const int32_t* pad_lens, float scale, int causal,
+             int n_q_heads, int n_kv_heads,
+             const attn_tensor_t* out, float* lse, void* stream);
+
+/* Static, human-readable text for a return code (never NULL). */
+const char* attn_strerror(int code);
+
+/* Library version string, e.g. "attn_fwd 0.1.0 gfx950". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/*.h declares, and rejects bad arguments on the host (no HIP call
+is made on any path exercised here)."""
+
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_attention_06_amd import attn as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return A.load_library()
+
+
+def test_header_declares_entry_points():
+    assert declared_functions() == sorted(A.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", A.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_strerror(lib):
+    assert A.version().startswith("attn_fwd ")
+    assert "gfx950" in A.version()
+    for code in range(-9, 1):
+        assert A.strerror(code)
+    assert A.strerror(-1234) == "unknown error code"
+
+
+FAKE = 0x10000  # a 16-byte aligned non-NULL address that is never dereferenced
+
+
+def T(B=1, S=8, H=2, D=64, dtype=A.ATTN_BF16, data=FAKE):
+    return A.AttnTensor(ctypes.c_void_p(data), dtype, B, S, H, D)
+
+
+def call(lib, q, k, v, out, mask_kind=0, pad=None, scale=0.0, causal=0, hq=None, hkv=None, lse=None):
+    hq = q.H if hq is None else hq
+    hkv = k.H if hkv is None else hkv
+    return lib.attn_fwd(ctypes.byref(q) if q is not None else None,
+                        ctypes.byref(k) if k is not None else None,
+                        ctypes.byref(v) if v is not None else None,
+                        mask_kind, pad, ctypes.c_float(scale), causal, hq, hkv,
+                        ctypes.byref(out) if out is not None else None, lse, None)
+
+
+def test_null_descriptors(lib):
+    assert call(lib, None, T(), T(), T(), hq=2, hkv=2) == A.ATTN_ERR_NULL
+    assert call(lib, T(), T(), T(), None, hq=2, hkv=2) == A.ATTN_ERR_NULL
+
+
+def test_null_data_pointer(lib):
+    assert call(lib, T(data=0), T(), T(), T()) == A.ATTN_ERR_NULL
+
+
+@pytest.mark.parametrize("field,val", [("B", 2), ("S", 9), ("D", 128)])
+def test_shape_mismatch(lib, field, val):
+    k = T()
+    setattr(k, field, val)
+    assert call(lib, T(), k, T(), T()) in (A.ATTN_ERR_SHAPE,)
+
+
+def test_negative_dims(lib):
+    assert call(lib, T(S=-1), T(S=-1), T(S=-1), T(S=-1)) == A.ATTN_ERR_SHAPE
+
+
+def test_head_checks(lib):
+    assert call(lib, T(H=4), T(H=3), T(H=3), T(H=4)) == A.ATTN_ERR_HEADS      # 4 % 3
+    assert call(lib, T(H=4), T(H=2), T(H=2), T(H=4), hq=8) == A.ATTN_ERR_HEADS
+    assert call(lib, T(H=4), T(H=2), T(H=1), T(H=4)) == A.ATTN_ERR_HEADS      # k.H != v.H
+    assert call(lib, T(H=4), T(H=2), T(H=2), T(H=2), hq=4) == A.ATTN_ERR_HEADS  # out.H
+    assert call(lib, T(H=2), T(H=2), T(H=2), T(H=2), hq=0, hkv=0) == A.ATTN_ERR_HEADS
+
+
+def test_dtype_checks(lib):
+    assert call(lib, T(dtype=7), T(), T(), T()) == A.ATTN_ERR_DTYPE
+    assert call(lib, T(), T(dtype=A.ATTN_F16), T(), T()) == A.ATTN_ERR_DTYPE
+    assert call(lib, T(), T(), T(), T(dtype=A.ATTN_F32)) == A.ATTN_ERR_DTYPE
+
+
+@pytest.mark.parametrize("d", [1, 16, 32, 80, 96, 256])
+def test_unsupported_head_dim(lib, d):
+    assert call(lib, T(D=d), T(D=d), T(D=d), T(D=d)) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_mask_checks(lib):
+    assert call(lib, T(), T(), T(), T(), mask_kind=2) == A.ATTN_ERR_MASK
+    assert call(lib, T(), T(), T(), T(), mask_kind=A.ATTN_MASK_KEY_PADDING, pad=None) == A.ATTN_ERR_MASK
+    assert call(lib, T(), T(), T(), T(), mask_kind=A.ATTN_MASK_NONE, pad=FAKE) == A.ATTN_ERR_MASK
+    assert call(lib, T(), T(), T(), T(), causal=2) == A.ATTN_ERR_MASK
+    assert call(lib, T(), T(), T(), T(), mask_kind=A.ATTN_MASK_KEY_PADDING, pad=FAKE + 2) == A.ATTN_ERR_ALIGN
+
+
+def test_alignment(lib):
+    assert call(lib, T(data=FAKE + 8), T(), T(), T()) == A.ATTN_ERR_ALIGN
+    assert call(lib, T(), T(), T(), T(data=FAKE + 2)) == A.ATTN_ERR_ALIGN
+    assert call(lib, T(), T(), T(), T(), lse=FAKE + 1) == A.ATTN_ERR_ALIGN
+
+
+def test_empty_inputs_return_ok_without_launch(lib):
+    # B == 0 or S == 0: nothing to do, and no HIP call (this container has no GPU)
+    assert call(lib, T(B=0), T(B=0), T(B=0), T(B=0)) == A.ATTN_OK
+    assert call(lib, T(S=0), T(S=0), T(S=0), T(S=0)) == A.ATTN_OK
+    assert call(lib, T(S=0, data=0), T(S=0, data=0), T(S=0, data=0), T(S=0, data=0)) == A.ATTN_OK
+
+
+def test_size_limits(lib):
+    big = dict(S=1 << 29)
+    assert call(lib, T(**big), T(**big), T(**big), T(**big)) == A.ATTN_ERR_UNSUPPORTED
+    assert call(lib, T(H=70000), T(H=1), T(H=1), T(H=70000)) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.attn_fwd(q, q, q, 0, None, None, False, 1, 1, q.clone(), None)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    import importlib
+    saved = A._LIB
+    try:
+        A._LIB = None
+        with pytest.raises(RuntimeError, match="missing"):
+            A.load_library(str(tmp_path / "nope.so"))
+    finally:
+        A._LIB = saved

@@ -1,0 +1,84 @@
+"""Parity bars between the HIP path and the fp64 oracle.
+
+The bars follow the stated requirement for this kernel: max-abs error
+<= 2e-2 and mean-abs error <= 2e-3 for bf16/fp16 inputs, max-abs <= 1e-5 for
+the fp32 path, and LSE within 1e-3.  Two readings where the literal bar
+cannot be met by any correct kernel (both derived, not tuned):
+
+* bf16 output rounding: when |O| >= 8 (Q/K/V outliers scaled by 20), one
+  bf16 half-ulp of the output alone is 2^-5 = 0.031 > 2e-2.  Such cases are
+  checked on |Δ| <= 2e-2 · max(1, |O_ref|) (an allclose with atol = rtol =
+  2e-2) together with the strict mean-abs and LSE bars; the strict max-abs
+  is reported next to it.
+* fp32 with heavy-tailed (Student-t, 2 dof) inputs: huge scores make the
+  softmax ill-conditioned, so fp32 rounding of a score (relative 2^-24 of
+  κ_i = scale · max_j Σ_d |q_id||k_jd|) moves P by that much times |V|.  The
+  bar is |Δ_id| <= max(1e-5, 4 · 2^-24 · (κ_i + D) · max_j |V_jd|).
+"""
+
+import numpy as np
+
+BAR = {
+    "bf16": dict(max_abs=2e-2, mean_abs=2e-3),
+    "fp16": dict(max_abs=2e-2, mean_abs=2e-3),
+    "fp32": dict(max_abs=1e-5, mean_abs=1e-5),
+}
+LSE_BAR = 1e-3
+
+
+def errors(out, ref):
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = np.abs(out - ref)
+    return dict(max_abs=float(d.max()) if d.size else 0.0,
+                mean_abs=float(d.mean()) if d.size else 0.0,
+                max_scaled=float((d / np.maximum(1.0, np.abs(ref))).max()) if d.size else 0.0)
+
+
+def lse_error(lse, ref):
+    lse = np.asarray(lse, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    both_ninf = np.isneginf(lse) & np.isneginf(ref)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref)), "rows with no visible key differ"
+    d = np.where(both_ninf, 0.0, np.abs(lse - ref))
+    assert np.all(np.isfinite(d)), "non-finite LSE"
+    return float(d.max()) if d.size else 0.0
+
+
+def assert_parity(out, ref, dtype, *, lse=None, lse_ref=None, scaled=False, what=""):
+    """Assert the stated bars; ``scaled`` selects the allclose reading for
+    bf16 outputs with large magnitudes (see module docstring)."""
+    out = np.asarray(out, dtype=np.float64)
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    e = errors(out, ref)
+    bar = BAR[dtype]
+    if scaled:
+        assert e["max_scaled"] <= bar["max_abs"], f"{what}: scaled err {e}"
+    else:
+        assert e["max_abs"] <= bar["max_abs"], f"{what}: {e}"
+    assert e["mean_abs"] <= bar["mean_abs"], f"{what}: {e}"
+    if lse is not None:
+        le = lse_error(lse, lse_ref)
+        e["lse"] = le
+        assert le <= LSE_BAR, f"{what}: lse err {le}"
+    return e
+
+
+def fp32_sensitivity_bound(q, k, v, scale, causal=False):
+    """Per-element bound for fp32 on ill-conditioned inputs (docstring)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    b_n, s, hq, d = q.shape
+    hkv = k.shape[2]
+    bound = np.zeros_like(q)
+    for b in range(b_n):
+        for h in range(hq):
+            g = h * hkv // hq
+            kap = scale * (np.abs(q[b, :, h, :]) @ np.abs(k[b, :, g, :]).T)
+            if causal:
+                kap = np.where(np.tril(np.ones((s, s), bool)), kap, 0.0)
+            kap_i = kap.max(axis=1)
+            vmax = np.abs(v[b, :, g, :]).max(axis=0)
+            bound[b, :, h, :] = 4 * 2.0 ** -24 * (kap_i[:, None] + d) * vmax[None, :]
+    return np.maximum(1e-5, bound)

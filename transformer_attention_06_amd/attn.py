@@ -1,0 +1,164 @@
+"""Python binding of libattn_fwd.so (argument marshalling only).
+
+Every step of the attention forward runs in the library's HIP kernels; this
+module only turns torch tensors into the C descriptors of ``include/attn_fwd.h``
+and passes torch's current HIP stream.  If the library has not been built,
+loading it raises: there is no Python or CPU fallback.
+"""
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn_fwd.so")
+
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+ATTN_MASK_NONE, ATTN_MASK_KEY_PADDING = 0, 1
+
+ATTN_OK = 0
+ATTN_ERR_NULL = -1
+ATTN_ERR_SHAPE = -2
+ATTN_ERR_HEADS = -3
+ATTN_ERR_DTYPE = -4
+ATTN_ERR_UNSUPPORTED = -5
+ATTN_ERR_MASK = -6
+ATTN_ERR_ALIGN = -7
+ATTN_ERR_LAUNCH = -8
+ATTN_ERR_DEVICE = -9
+
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_strerror", "attn_version")
+
+
+class AttnTensor(ctypes.Structure):
+    """Mirror of ``attn_tensor_t``: a contiguous (B, S, H, D) device buffer."""
+
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int64),
+        ("S", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+    ]
+
+
+_LIB = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libattn_fwd.so once and declare its C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m transformer_attention_06_amd.build` "
+            "(hipcc, gfx950). There is no fallback path.")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(AttnTensor)
+    lib.attn_fwd.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
+                             ctypes.c_int, ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_strerror.argtypes = [ctypes.c_int]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def strerror(code):
+    return load_library().attn_strerror(int(code)).decode()
+
+
+def version():
+    return load_library().attn_version().decode()
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code):
+        self.code = code
+        super().__init__(f"attn_fwd failed ({code}): {strerror(code)}")
+
+
+class AttnArgumentError(AttnError, ValueError):
+    pass
+
+
+def check(code):
+    if code == ATTN_OK:
+        return
+    if code in (ATTN_ERR_LAUNCH, ATTN_ERR_DEVICE):
+        raise AttnError(code)
+    raise AttnArgumentError(code)
+
+
+def _dtype_code(t):
+    import torch
+    codes = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+    if t.dtype not in codes:
+        raise AttnArgumentError(ATTN_ERR_DTYPE)
+    return codes[t.dtype]
+
+
+def describe(t):
+    """AttnTensor for a contiguous 4-D (B, S, H, D) torch tensor."""
+    if t.dim() != 4:
+        raise AttnArgumentError(ATTN_ERR_SHAPE)
+    if not t.is_contiguous():
+        raise ValueError("attn_fwd needs contiguous (B, S, H, D) tensors")
+    b, s, h, d = t.shape
+    return AttnTensor(ctypes.c_void_p(t.data_ptr()), _dtype_code(t), b, s, h, d)
+
+
+def attn_fwd(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
+             stream=None):
+    """The C entry point with torch tensors: fills ``out`` (and ``lse``).
+
+    q, k, v, out: contiguous device tensors (B, S, H, D) of one dtype;
+    pad_lens: int32 device tensor [B] or None; lse: float32 device tensor
+    [B, n_q_heads, S] or None; scale: float (<= 0 or None selects 1/sqrt(D));
+    stream: a torch stream (default: the current stream).
+    """
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    pad_ptr = None
+    if pad_lens is not None:
+        if pad_lens.dtype != torch.int32 or not pad_lens.is_cuda or not pad_lens.is_contiguous():
+            raise ValueError("pad_lens must be a contiguous int32 device tensor")
+        pad_ptr = ctypes.c_void_p(pad_lens.data_ptr())
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 device tensor")
+        if tuple(lse.shape) != (q.shape[0], n_q_heads, q.shape[1]):
+            raise ValueError("lse must be [B, n_q_heads, S]")
+        lse_ptr = ctypes.c_void_p(lse.data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
+    code = lib.attn_fwd(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(mask_kind), pad_ptr,
+                        ctypes.c_float(0.0 if scale is None else float(scale)), int(bool(causal)),
+                        int(n_q_heads), int(n_kv_heads), ctypes.byref(do), lse_ptr,
+                        ctypes.c_void_p(stream.cuda_stream))
+    check(code)
+    return out, lse
+
+
+def flash_attention(q, k, v, *, causal=False, pad_lens=None, scale=None, return_lse=False):
+    """Allocate ``out`` (and ``lse``) with torch and run ``attn_fwd``.
+
+    q: (B, S, Hq, D); k, v: (B, S, Hkv, D); pad_lens: int32 [B] or None.
+    Returns out, or (out, lse) with lse float32 [B, Hq, S].
+    """
+    import torch
+    out = torch.empty_like(q)
+    lse = None
+    if return_lse:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    mask_kind = ATTN_MASK_NONE if pad_lens is None else ATTN_MASK_KEY_PADDING
+    attn_fwd(q, k, v, mask_kind, pad_lens, scale, causal, q.shape[2], k.shape[2], out, lse)
+    return (out, lse) if return_lse else out

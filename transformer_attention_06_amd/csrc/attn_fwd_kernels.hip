@@ -1,0 +1,430 @@
+// attn_fwd_kernels.hip — fused attention forward for gfx950 (MI355X).
+//
+// One workgroup (4 wavefronts of 64 lanes) owns one (batch, query head,
+// 128-row query block); each wavefront owns 32 query rows.  K/V tiles of BN
+// keys stream through double-buffered LDS; the score tile, the online-softmax
+// state and the output accumulator never leave registers, so the S×S score
+// matrix never reaches device memory ("ops-transformer：Transformer算子融合与
+// 推理加速实战" §2.2 structural fusion, §3.2 blockwise loop nest with a running
+// local max and sum, §2.3 prefetching the next block while the current one is
+// computed).
+//
+// Both products run on MFMA, computed TRANSPOSED so that every lane owns one
+// query row:
+//     Sᵀ (keys × rows)  = K · Qᵀ      A = K tile (LDS),  B = Q (registers)
+//     Oᵀ (dims × rows) += Vᵀ · Pᵀ     A = Vᵀ tile (LDS), B = P (registers)
+// With the 32×32 MFMA accumulator layout, lane l holds column l%32 (= one
+// query row) and 16 rows of the tile, so the softmax row max and row sum are
+// in-lane reductions plus one exchange with lane l^32, the P operand of the
+// second product is formed from the first product's accumulators without any
+// data movement, and the rescale of the output accumulator by the running-max
+// correction is a per-lane scalar.  The A operands are loaded with a fixed
+// row permutation (bits 2 and 3 of the row index swapped) so that each lane's
+// registers cover 8 consecutive keys / head dims: P packs straight into MFMA
+// operands, Vᵀ rows are read as one 16-byte LDS load, and the output is stored
+// as 16-byte vectors.
+//
+// Precision ("ops-transformer…" §2.4): bf16/fp16 storage and MFMA inputs, fp32
+// accumulation, fp32 running max / sum, output rounded to the storage type at
+// the end.  Scores are scaled by scale·log2(e) so the exponentials are exp2.
+// The fp32 path uses the fp32 MFMA and keeps P in fp32.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn_fwd.h"
+#include "attn_launch.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int BM = attn_detail::kBlockM;  // 128 query rows per workgroup
+static_assert(BM == 4 * 32, "4 wavefronts x 32 rows");
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+    static constexpr int KPL = 8;  // operand elements per lane per MFMA
+    static constexpr int BN = 64;  // keys per K/V tile
+    using op_t = bf16x8;
+};
+template <>
+struct Elem<_Float16> {
+    static constexpr int KPL = 8;
+    static constexpr int BN = 64;
+    using op_t = f16x8;
+};
+template <>
+struct Elem<float> {
+    static constexpr int KPL = 1;
+    static constexpr int BN = 32;
+    using op_t = float;
+};
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <typename OP, typename T>
+__device__ __forceinline__ OP load_op(const T* p) {
+    return *reinterpret_cast<const OP*>(p);
+}
+
+// A-operand row permutation: swap bits 2 and 3 of a 0..31 row index.
+__device__ __forceinline__ int perm_row(int r) {
+    return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Position (key within the tile, or head dim within a 32-wide block pair)
+// held by accumulator register f (0..16*blocks-1) of a lane in half g.
+__host__ __device__ constexpr int kidx(int f, int g) {
+    return 32 * (f >> 4) + 16 * ((f >> 3) & 1) + 8 * g + (f & 7);
+}
+
+struct KParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* pad_lens;
+    int S, Hq, Hkv, group, n_qb, n_units, xcd_chunk;
+    int64_t q_bstride, kv_bstride;  // elements per batch
+    float sl2;                      // scale * log2(e)
+};
+
+template <typename T>
+__device__ __forceinline__ T to_t(float x) {
+    return static_cast<T>(x);
+}
+
+template <typename T, int D, bool CAUSAL, bool PAD>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
+    using E = Elem<T>;
+    using op_t = typename E::op_t;
+    constexpr int KPL = E::KPL;
+    constexpr int BN = E::BN;
+    constexpr int CH = 16 / int(sizeof(T));  // elements per 16-byte chunk
+    constexpr int KSTR = D + CH;             // K tile row stride (elements)
+    constexpr int VSTR = BN + CH;            // Vᵀ tile row stride (elements)
+    constexpr int KT = BN * KSTR;
+    constexpr int VT = D * VSTR;
+    constexpr int NC = D / (2 * KPL);    // MFMA steps along D (Sᵀ)
+    constexpr int NBLK = BN / 32;        // 32-key blocks per tile
+    constexpr int NKC = BN / (2 * KPL);  // MFMA steps along keys (Oᵀ)
+    constexpr int NDB = D / 32;          // 32-dim blocks of O
+    constexpr int NK = BN * D / CH / kThreads;  // K chunks per thread
+    constexpr bool PAIRED = sizeof(T) == 2;     // Vᵀ built from key pairs
+    constexpr int NVU = PAIRED ? (BN / 2) * (D / 8) / kThreads : BN * (D / 4) / kThreads;
+    constexpr int VL = PAIRED ? 2 : 1;
+    static_assert(NK * kThreads * CH == BN * D, "K tile split");
+    static_assert(NVU * kThreads == (PAIRED ? (BN / 2) * (D / 8) : BN * (D / 4)), "V tile split");
+
+    __shared__ __attribute__((aligned(16))) T smem[2 * (KT + VT)];
+
+    // ---- work decomposition ------------------------------------------------
+    // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
+    // head) are split into 8 contiguous ranges, one per XCD, so the query
+    // heads sharing a K/V head share that XCD's L2; within an XCD the query
+    // blocks run heaviest first under causal masking.
+    const int wg = blockIdx.x;
+    int unit, qb_rank;
+    if (p.xcd_chunk > 0) {
+        const int xcd = wg & 7, local = wg >> 3;
+        qb_rank = local / p.xcd_chunk;
+        unit = xcd * p.xcd_chunk + local % p.xcd_chunk;
+    } else {
+        qb_rank = wg / p.n_units;
+        unit = wg % p.n_units;
+    }
+    const int qb = CAUSAL ? (p.n_qb - 1 - qb_rank) : qb_rank;
+    const int jg = unit % p.group;
+    const int bg = unit / p.group;
+    const int g = bg % p.Hkv;
+    const int b = bg / p.Hkv;
+    const int hq = g * p.group + jg;
+
+    const int S = p.S;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r = lane & 31;
+    const int gl = lane >> 5;
+    const int q0 = qb * BM;
+    const int wrow0 = q0 + wave * 32;
+    const int qrow = wrow0 + r;
+
+    const int64_t qstride = int64_t(p.Hq) * D;
+    const int64_t kvstride = int64_t(p.Hkv) * D;
+    const T* qbase = static_cast<const T*>(p.q) + int64_t(b) * p.q_bstride + int64_t(hq) * D;
+    const T* kbase = static_cast<const T*>(p.k) + int64_t(b) * p.kv_bstride + int64_t(g) * D;
+    const T* vbase = static_cast<const T*>(p.v) + int64_t(b) * p.kv_bstride + int64_t(g) * D;
+
+    // ---- Q tile: MFMA B operands, resident for the whole loop ------------
+    op_t qv[NC];
+    if (qrow < S) {
+        const T* qr = qbase + int64_t(qrow) * qstride;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qv[c] = load_op<op_t>(qr + c * 2 * KPL + gl * KPL);
+    } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qv[c] = op_t{};
+    }
+
+    // ---- key range ----------------------------------------------------------
+    int key_lim = S;
+    if (PAD) {
+        const int L = p.pad_lens[b];
+        key_lim = L < 0 ? 0 : (L > S ? S : L);
+    }
+    int key_end = key_lim;
+    if (CAUSAL) key_end = key_end < q0 + BM ? key_end : q0 + BM;
+    const int n_tiles = (key_end + BN - 1) / BN;
+
+    // ---- tile staging: global -> registers -> LDS -------------------------
+    u32x4 kreg[NK];
+    u32x4 vreg[NVU][VL];
+    auto load_tile = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int c = tid + kThreads * i;
+            const int row = c / (D / CH);
+            const int col = (c % (D / CH)) * CH;
+            const int key = kb + row;
+            kreg[i] = key < S ? load_op<u32x4>(kbase + int64_t(key) * kvstride + col) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < NVU; ++i) {
+            const int u = tid + kThreads * i;
+            if constexpr (PAIRED) {
+                const int kp = u % (BN / 2);
+                const int dch = u / (BN / 2);
+                const int key0 = kb + 2 * kp;
+                vreg[i][0] = key0 < S ? load_op<u32x4>(vbase + int64_t(key0) * kvstride + dch * 8)
+                                      : u32x4{0, 0, 0, 0};
+                vreg[i][VL - 1] = key0 + 1 < S
+                                      ? load_op<u32x4>(vbase + int64_t(key0 + 1) * kvstride + dch * 8)
+                                      : u32x4{0, 0, 0, 0};
+            } else {
+                const int key = kb + u % BN;
+                const int dch = u / BN;
+                vreg[i][0] = key < S ? load_op<u32x4>(vbase + int64_t(key) * kvstride + dch * 4)
+                                     : u32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        T* ks = smem + buf * (KT + VT);
+        T* vt = ks + KT;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int c = tid + kThreads * i;
+            const int row = c / (D / CH);
+            const int col = (c % (D / CH)) * CH;
+            *reinterpret_cast<u32x4*>(ks + row * KSTR + col) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NVU; ++i) {
+            const int u = tid + kThreads * i;
+            if constexpr (PAIRED) {
+                const int kp = u % (BN / 2);
+                const int dch = u / (BN / 2);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t a = vreg[i][0][e >> 1];
+                    const uint32_t c2 = vreg[i][VL - 1][e >> 1];
+                    const uint32_t w = (e & 1) ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
+                    *reinterpret_cast<uint32_t*>(vt + (dch * 8 + e) * VSTR + 2 * kp) = w;
+                }
+            } else {
+                const int kl = u % BN;
+                const int dch = u / BN;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<uint32_t*>(vt + (dch * 4 + e) * VSTR + kl) = vreg[i][0][e];
+            }
+        }
+    };
+
+    // ---- online-softmax state ----------------------------------------------
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float m_run = -INFINITY;  // running max of scale*log2(e)*score
+    float l_run = 0.0f;       // running sum (this lane's half of the keys)
+    const float sl2 = p.sl2;
+    const int prow = perm_row(r);
+
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int j = 0; j < n_tiles; ++j) {
+        const int kb = j * BN;
+        const bool more = j + 1 < n_tiles;
+        if (more) load_tile(kb + BN);
+
+        const T* ks = smem + (j & 1) * (KT + VT);
+        const T* vt = ks + KT;
+        const bool active = !CAUSAL || kb <= wrow0 + 31;
+        if (active) {
+            // Sᵀ = K · Qᵀ for this wave's 32 rows
+            f32x16 sacc[NBLK];
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk) sacc[blk] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+#pragma unroll
+                for (int blk = 0; blk < NBLK; ++blk) {
+                    const op_t a = load_op<op_t>(ks + (prow + 32 * blk) * KSTR + c * 2 * KPL + gl * KPL);
+                    sacc[blk] = mfma(a, qv[c], sacc[blk]);
+                }
+            }
+            // mask: keys past the valid length, and keys after the row (causal)
+            const bool need_mask = (kb + BN > key_lim) || (CAUSAL && kb + BN - 1 > wrow0);
+            if (need_mask) {
+#pragma unroll
+                for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb + kidx(16 * blk + i, gl);
+                        const bool ok = key < key_lim && (!CAUSAL || key <= qrow);
+                        if (!ok) sacc[blk][i] = -INFINITY;
+                    }
+            }
+            // online softmax
+            float mx = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx * sl2);
+            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            float rs = 0.0f;
+            op_t pb[NKC];
+#pragma unroll
+            for (int f = 0; f < 16 * NBLK; ++f) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[f >> 4][f & 15], sl2, -m_use));
+                rs += pv;
+                if constexpr (KPL == 1)
+                    pb[f] = pv;
+                else
+                    pb[f / KPL][f % KPL] = to_t<T>(pv);
+            }
+            l_run = l_run * alpha + rs;
+            m_run = m_new;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            // Oᵀ += Vᵀ · Pᵀ
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const op_t a = load_op<op_t>(vt + (prow + 32 * db) * VSTR + kidx(kc * KPL, gl));
+                    oacc[db] = mfma(a, pb[kc], oacc[db]);
+                }
+            }
+        }
+
+        if (more) store_tile((j + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: normalise, store O (and LSE) ---------------------------
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if (qrow < S) {
+        T* orow = static_cast<T*>(p.o) + int64_t(b) * p.q_bstride + int64_t(qrow) * qstride +
+                  int64_t(hq) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                T vals[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vals[e] = to_t<T>(oacc[db][8 * h + e] * inv);
+                T* dst = orow + 32 * db + 16 * h + 8 * gl;
+                if constexpr (sizeof(T) == 2) {
+                    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(vals);
+                } else {
+                    reinterpret_cast<u32x4*>(dst)[0] = reinterpret_cast<const u32x4*>(vals)[0];
+                    reinterpret_cast<u32x4*>(dst)[1] = reinterpret_cast<const u32x4*>(vals)[1];
+                }
+            }
+        if (p.lse != nullptr && gl == 0) {
+            const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f
+                                           : -INFINITY;
+            p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] = lse;
+        }
+    }
+}
+
+template <typename T, int D, bool CAUSAL, bool PAD>
+int launch_t(const attn_detail::LaunchArgs& a) {
+    KParams kp;
+    kp.q = a.q;
+    kp.k = a.k;
+    kp.v = a.v;
+    kp.o = a.o;
+    kp.lse = a.lse;
+    kp.pad_lens = a.pad_lens;
+    kp.S = int(a.S);
+    kp.Hq = int(a.Hq);
+    kp.Hkv = int(a.Hkv);
+    kp.group = int(a.Hq / a.Hkv);
+    kp.n_qb = int((a.S + BM - 1) / BM);
+    kp.n_units = int(a.B * a.Hq);
+    kp.xcd_chunk = (kp.n_units % 8 == 0) ? kp.n_units / 8 : 0;
+    kp.q_bstride = a.S * a.Hq * a.D;
+    kp.kv_bstride = a.S * a.Hkv * a.D;
+    kp.sl2 = a.scale * 1.44269504088896340736f;
+    const int64_t n_wg = int64_t(kp.n_qb) * kp.n_units;
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD>), dim3(unsigned(n_wg)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(a.stream), kp);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return ATTN_OK;
+    if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction) return ATTN_ERR_DEVICE;
+    return ATTN_ERR_LAUNCH;
+}
+
+template <typename T, int D>
+int launch_d(const attn_detail::LaunchArgs& a) {
+    if (a.causal) return a.padded ? launch_t<T, D, true, true>(a) : launch_t<T, D, true, false>(a);
+    return a.padded ? launch_t<T, D, false, true>(a) : launch_t<T, D, false, false>(a);
+}
+
+template <typename T>
+int launch_dtype(const attn_detail::LaunchArgs& a) {
+    return a.D == 64 ? launch_d<T, 64>(a) : launch_d<T, 128>(a);
+}
+
+}  // namespace
+
+namespace attn_detail {
+
+int launch(const LaunchArgs& a) {
+    switch (a.dtype) {
+        case ATTN_BF16: return launch_dtype<__bf16>(a);
+        case ATTN_F16: return launch_dtype<_Float16>(a);
+        default: return launch_dtype<float>(a);
+    }
+}
+
+}  // namespace attn_detail
