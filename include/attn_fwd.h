@@ -108,7 +108,8 @@ enum {
  *               (-inf for a row with no visible key), or NULL to skip it.
  *   stream      hipStream_t to enqueue on (NULL = default stream).
  *
- * Limits: S < 2^31 / 4, B*S*H*D < 2^62, Hq <= 65535.
+ * Limits: S < 2^29, Hq <= 65535, and one batch of K (or V) below 2 GiB:
+ * S * n_kv_heads * D * sizeof(element) < 2^31 (ATTN_ERR_UNSUPPORTED).
  * Returns ATTN_OK or one of the negative codes above.
  */
 int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,

@@ -61,6 +61,9 @@ extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const at
     // Total element counts must stay far from int64 overflow.
     const double elems = double(B) * double(S) * double(n_q_heads) * double(D);
     if (elems >= 4.0e18) return ATTN_ERR_UNSUPPORTED;
+    // K/V of one batch are addressed with 32-bit byte offsets on the device.
+    const int64_t esize = q->dtype == ATTN_F32 ? 4 : 2;
+    if (S * int64_t(n_kv_heads) * D * esize >= (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
     const int64_t n_qb = (S + attn_detail::kBlockM - 1) / attn_detail::kBlockM;
     const double wgs = double(n_qb) * double(n_q_heads) * double(B);
     if (wgs >= 2147483647.0) return ATTN_ERR_UNSUPPORTED;

@@ -21,8 +21,10 @@
 // correction is a per-lane scalar.  The A operands are loaded with a fixed
 // row permutation (bits 2 and 3 of the row index swapped) so that each lane's
 // registers cover 8 consecutive keys / head dims: P packs straight into MFMA
-// operands, Vᵀ rows are read as one 16-byte LDS load, and the output is stored
-// as 16-byte vectors.
+// operands and the output is stored as 16-byte vectors.  K and V both sit in
+// LDS row-major (key-major, as in memory); the Vᵀ operand is read with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16), whose 4×16 transpose per
+// 16-lane group lines up with the same bit-2/3 row permutation.
 //
 // Precision ("ops-transformer…" §2.4): bf16/fp16 storage and MFMA inputs, fp32
 // accumulation, fp32 running max / sum, output rounded to the storage type at
@@ -83,6 +85,54 @@ __device__ __forceinline__ OP load_op(const T* p) {
     return *reinterpret_cast<const OP*>(p);
 }
 
+// Buffer resource over [base, base + bytes): loads at offsets at or past the
+// end return zero, which zero-fills K/V rows beyond the sequence end without
+// branches.  Word 3 is the gfx9-family default data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), 0);
+}
+
+// Combine a value with the one held by lane l^32 (the other half of the
+// same query row): one cross-half swap instead of an LDS permute.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The running max is only raised when a row's new tile max exceeds it by
+// more than this many powers of two; otherwise the stale max is kept, the
+// exponentials stay below 2^8 and the output accumulator needs no rescale.
+constexpr float kRescaleLog2 = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Transposing LDS read: in each 16-lane group, lane 4j+q names an 8-byte
+// piece (4 elements of one row); lane 4q+c receives element c of the pieces
+// named by lanes 4j+q, j = 0..3 (a 4-row × 16-column block, transposed).
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+    typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
+}
+
+// Sum of the two 16-bit probabilities in a packed pair, accumulated in fp32
+// (dot product with (1, 1)): the row sum is taken over exactly the rounded
+// values that enter the P·V product.
+__device__ __forceinline__ float sum2(bf16x2 p, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(p, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+}
+__device__ __forceinline__ float sum2(f16x2 p, float acc) {
+    return __builtin_amdgcn_fdot2(p, f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+}
+
 // A-operand row permutation: swap bits 2 and 3 of a 0..31 row index.
 __device__ __forceinline__ int perm_row(int r) {
     return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -111,29 +161,23 @@ __device__ __forceinline__ T to_t(float x) {
     return static_cast<T>(x);
 }
 
-template <typename T, int D, bool CAUSAL, bool PAD>
+template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
     constexpr int KPL = E::KPL;
     constexpr int BN = E::BN;
     constexpr int CH = 16 / int(sizeof(T));  // elements per 16-byte chunk
-    constexpr int KSTR = D + CH;             // K tile row stride (elements)
-    constexpr int VSTR = BN + CH;            // Vᵀ tile row stride (elements)
-    constexpr int KT = BN * KSTR;
-    constexpr int VT = D * VSTR;
+    constexpr int KSTR = D + CH;             // K/V tile row stride (elements)
+    constexpr int KT = BN * KSTR;            // one K (or V) tile
     constexpr int NC = D / (2 * KPL);    // MFMA steps along D (Sᵀ)
     constexpr int NBLK = BN / 32;        // 32-key blocks per tile
     constexpr int NKC = BN / (2 * KPL);  // MFMA steps along keys (Oᵀ)
     constexpr int NDB = D / 32;          // 32-dim blocks of O
-    constexpr int NK = BN * D / CH / kThreads;  // K chunks per thread
-    constexpr bool PAIRED = sizeof(T) == 2;     // Vᵀ built from key pairs
-    constexpr int NVU = PAIRED ? (BN / 2) * (D / 8) / kThreads : BN * (D / 4) / kThreads;
-    constexpr int VL = PAIRED ? 2 : 1;
-    static_assert(NK * kThreads * CH == BN * D, "K tile split");
-    static_assert(NVU * kThreads == (PAIRED ? (BN / 2) * (D / 8) : BN * (D / 4)), "V tile split");
+    constexpr int NK = BN * D / CH / kThreads;  // 16-byte chunks per thread per tile
+    static_assert(NK * kThreads * CH == BN * D, "tile split");
 
-    __shared__ __attribute__((aligned(16))) T smem[2 * (KT + VT)];
+    __shared__ __attribute__((aligned(16))) T smem[2 * 2 * KT];  // [buf][K|V][BN][KSTR]
 
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
@@ -195,67 +239,38 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     const int n_tiles = (key_end + BN - 1) / BN;
 
     // ---- tile staging: global -> registers -> LDS -------------------------
+    // Buffer loads address the (batch, kv head) slice; rows at or past S fall
+    // outside the resource and read as zero.  Per-thread offsets are fixed;
+    // the tile position is a scalar offset.
+    const uint32_t kv_bytes = uint32_t((int64_t(S) * kvstride - int64_t(g) * D) * int64_t(sizeof(T)));
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kv_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, kv_bytes);
+    const uint32_t row_bytes = uint32_t(kvstride * int64_t(sizeof(T)));
+    uint32_t koff[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        const int c = tid + kThreads * i;
+        koff[i] = uint32_t(c / (D / CH)) * row_bytes + uint32_t((c % (D / CH)) * CH * int(sizeof(T)));
+    }
     u32x4 kreg[NK];
-    u32x4 vreg[NVU][VL];
+    u32x4 vreg[NK];
     auto load_tile = [&](int kb) {
+        const uint32_t soff = uint32_t(kb) * row_bytes;
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
-            const int c = tid + kThreads * i;
-            const int row = c / (D / CH);
-            const int col = (c % (D / CH)) * CH;
-            const int key = kb + row;
-            kreg[i] = key < S ? load_op<u32x4>(kbase + int64_t(key) * kvstride + col) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < NVU; ++i) {
-            const int u = tid + kThreads * i;
-            if constexpr (PAIRED) {
-                const int kp = u % (BN / 2);
-                const int dch = u / (BN / 2);
-                const int key0 = kb + 2 * kp;
-                vreg[i][0] = key0 < S ? load_op<u32x4>(vbase + int64_t(key0) * kvstride + dch * 8)
-                                      : u32x4{0, 0, 0, 0};
-                vreg[i][VL - 1] = key0 + 1 < S
-                                      ? load_op<u32x4>(vbase + int64_t(key0 + 1) * kvstride + dch * 8)
-                                      : u32x4{0, 0, 0, 0};
-            } else {
-                const int key = kb + u % BN;
-                const int dch = u / BN;
-                vreg[i][0] = key < S ? load_op<u32x4>(vbase + int64_t(key) * kvstride + dch * 4)
-                                     : u32x4{0, 0, 0, 0};
-            }
+            kreg[i] = buf_load16(krs, koff[i], soff);
+            vreg[i] = buf_load16(vrs, koff[i], soff);
         }
     };
     auto store_tile = [&](int buf) {
-        T* ks = smem + buf * (KT + VT);
-        T* vt = ks + KT;
+        T* ks = smem + buf * (2 * KT);
+        T* vs = ks + KT;
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int c = tid + kThreads * i;
-            const int row = c / (D / CH);
-            const int col = (c % (D / CH)) * CH;
-            *reinterpret_cast<u32x4*>(ks + row * KSTR + col) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < NVU; ++i) {
-            const int u = tid + kThreads * i;
-            if constexpr (PAIRED) {
-                const int kp = u % (BN / 2);
-                const int dch = u / (BN / 2);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t a = vreg[i][0][e >> 1];
-                    const uint32_t c2 = vreg[i][VL - 1][e >> 1];
-                    const uint32_t w = (e & 1) ? ((a >> 16) | (c2 & 0xffff0000u)) : ((a & 0xffffu) | (c2 << 16));
-                    *reinterpret_cast<uint32_t*>(vt + (dch * 8 + e) * VSTR + 2 * kp) = w;
-                }
-            } else {
-                const int kl = u % BN;
-                const int dch = u / BN;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    *reinterpret_cast<uint32_t*>(vt + (dch * 4 + e) * VSTR + kl) = vreg[i][0][e];
-            }
+            const int off = (c / (D / CH)) * KSTR + (c % (D / CH)) * CH;
+            *reinterpret_cast<u32x4*>(ks + off) = kreg[i];
+            *reinterpret_cast<u32x4*>(vs + off) = vreg[i];
         }
     };
 
@@ -264,14 +279,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY;  // running max of scale*log2(e)*score
-    float l_run = 0.0f;       // running sum (this lane's half of the keys)
+    float l_run = 0.0f;       // running sum of the rounded P (this lane's half of the keys)
+    float l_lse = 0.0f;       // running sum of the unrounded P, for the LSE output
     const float sl2 = p.sl2;
     const int prow = perm_row(r);
+    // Transposing-read address of this lane inside a 4-key × 32-dim block:
+    // row (r & 15) >> 2, columns 16·(r >> 4) + 4·swap01(r & 3) (see lds_read_tr16).
+    const int tr_off = ((r & 15) >> 2) * KSTR + 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
 
     if (n_tiles > 0) {
         load_tile(0);
         store_tile(0);
     }
+    // All loads issued so far (Q and the first tile) are complete here on
+    // every path; saying so keeps the loop free of waits on them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     for (int j = 0; j < n_tiles; ++j) {
@@ -279,8 +301,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
         const bool more = j + 1 < n_tiles;
         if (more) load_tile(kb + BN);
 
-        const T* ks = smem + (j & 1) * (KT + VT);
-        const T* vt = ks + KT;
+        const T* ks = smem + (j & 1) * (2 * KT);
+        const T* vs = ks + KT;
         const bool active = !CAUSAL || kb <= wrow0 + 31;
         if (active) {
             // Sᵀ = K · Qᵀ for this wave's 32 rows
@@ -313,31 +335,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
             for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx * sl2);
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            mx = max_xor32(mx) * sl2;
+            // raise the running max only when some row of the wave needs it
+            if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+                if constexpr (LSE) l_lse *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
             float rs = 0.0f;
+            float rs_lse = 0.0f;
             op_t pb[NKC];
 #pragma unroll
             for (int f = 0; f < 16 * NBLK; ++f) {
                 const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[f >> 4][f & 15], sl2, -m_use));
-                rs += pv;
-                if constexpr (KPL == 1)
+                if constexpr (KPL == 1) {
                     pb[f] = pv;
-                else
+                    rs += pv;
+                } else {
                     pb[f / KPL][f % KPL] = to_t<T>(pv);
+                    if constexpr (LSE) rs_lse += pv;
+                }
             }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
+            if constexpr (KPL == 1) rs_lse = rs;
+            if constexpr (KPL != 1) {
+                typedef T t2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+                for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                    for (int e = 0; e < KPL; e += 2)
+                        rs = sum2(t2{pb[kc][e], pb[kc][e + 1]}, rs);
+            }
+            l_run += rs;
+            if constexpr (LSE) l_lse += rs_lse;
             // Oᵀ += Vᵀ · Pᵀ
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const op_t a = load_op<op_t>(vt + (prow + 32 * db) * VSTR + kidx(kc * KPL, gl));
+                    op_t a;
+                    if constexpr (KPL == 1) {
+                        a = vs[kidx(kc, gl) * KSTR + 32 * db + prow];
+                    } else {
+                        const T* src = vs + (16 * kc + 8 * gl) * KSTR + 32 * db + tr_off;
+                        const s16x4 lo = lds_read_tr16(src);
+                        const s16x4 hi = lds_read_tr16(src + 4 * KSTR);
+                        a = __builtin_bit_cast(op_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
                     oacc[db] = mfma(a, pb[kc], oacc[db]);
                 }
             }
@@ -348,7 +396,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     }
 
     // ---- epilogue: normalise, store O (and LSE) ---------------------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = sum_xor32(l_run);
+    const float l_e = LSE ? sum_xor32(l_lse) : 0.0f;
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if (qrow < S) {
         T* orow = static_cast<T*>(p.o) + int64_t(b) * p.q_bstride + int64_t(qrow) * qstride +
@@ -368,15 +417,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
                     reinterpret_cast<u32x4*>(dst)[1] = reinterpret_cast<const u32x4*>(vals)[1];
                 }
             }
-        if (p.lse != nullptr && gl == 0) {
-            const float lse = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f
-                                           : -INFINITY;
+        if (LSE && gl == 0) {
+            const float lse = l_e > 0.0f ? (m_run + __builtin_amdgcn_logf(l_e)) * 0.69314718055994530942f
+                                         : -INFINITY;
             p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] = lse;
         }
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool PAD>
+template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
 int launch_t(const attn_detail::LaunchArgs& a) {
     KParams kp;
     kp.q = a.q;
@@ -396,7 +445,7 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     kp.kv_bstride = a.S * a.Hkv * a.D;
     kp.sl2 = a.scale * 1.44269504088896340736f;
     const int64_t n_wg = int64_t(kp.n_qb) * kp.n_units;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD>), dim3(unsigned(n_wg)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD, LSE>), dim3(unsigned(n_wg)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(a.stream), kp);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return ATTN_OK;
@@ -404,10 +453,15 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     return ATTN_ERR_LAUNCH;
 }
 
+template <typename T, int D, bool LSE>
+int launch_l(const attn_detail::LaunchArgs& a) {
+    if (a.causal) return a.padded ? launch_t<T, D, true, true, LSE>(a) : launch_t<T, D, true, false, LSE>(a);
+    return a.padded ? launch_t<T, D, false, true, LSE>(a) : launch_t<T, D, false, false, LSE>(a);
+}
+
 template <typename T, int D>
 int launch_d(const attn_detail::LaunchArgs& a) {
-    if (a.causal) return a.padded ? launch_t<T, D, true, true>(a) : launch_t<T, D, true, false>(a);
-    return a.padded ? launch_t<T, D, false, true>(a) : launch_t<T, D, false, false>(a);
+    return a.lse != nullptr ? launch_l<T, D, true>(a) : launch_l<T, D, false>(a);
 }
 
 template <typename T>
