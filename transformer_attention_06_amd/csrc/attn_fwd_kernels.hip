@@ -161,29 +161,59 @@ __device__ __forceinline__ T to_t(float x) {
     return static_cast<T>(x);
 }
 
+// XOR swizzle of the 16-byte slots of a K/V tile row (NS slots per row).
+// With 64 LDS banks, this makes the three access patterns of the kernel
+// conflict-free: 16-lane row writes, the K-operand reads (16 permuted rows,
+// one slot each) and the transposing V reads (4 consecutive rows, 32 bytes
+// each, two 16-lane groups side by side).
+template <int NS>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (NS >= 16)
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    else
+        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+template <typename T>
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, T* lds_dst, uint32_t voff) {
+    // one 16-byte global load per lane, written to lds_dst + 16 * lane
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_dst), 16,
+                                             voff, 0, 0, 0);
+}
+
+// 16-bit instances keep two wavefronts per SIMD (two workgroups per CU); the
+// fp32 instances hold twice the operand registers and run one.
 template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_kernel(KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
     constexpr int KPL = E::KPL;
     constexpr int BN = E::BN;
-    constexpr int CH = 16 / int(sizeof(T));  // elements per 16-byte chunk
-    constexpr int KSTR = D + CH;             // K/V tile row stride (elements)
-    constexpr int KT = BN * KSTR;            // one K (or V) tile
-    constexpr int NC = D / (2 * KPL);    // MFMA steps along D (Sᵀ)
-    constexpr int NBLK = BN / 32;        // 32-key blocks per tile
-    constexpr int NKC = BN / (2 * KPL);  // MFMA steps along keys (Oᵀ)
-    constexpr int NDB = D / 32;          // 32-dim blocks of O
-    constexpr int NK = BN * D / CH / kThreads;  // 16-byte chunks per thread per tile
-    static_assert(NK * kThreads * CH == BN * D, "tile split");
+    constexpr int ES = int(sizeof(T));
+    constexpr int CH = 16 / ES;            // elements per 16-byte slot
+    constexpr int NS = D / CH;             // slots per tile row
+    constexpr int ROW_B = D * ES;          // bytes per tile row
+    constexpr int TILE_E = BN * D;         // elements per K (or V) tile
+    constexpr int NLD = BN * ROW_B / 4096; // 1 KiB direct loads per wave per tile
+    static_assert(NLD * 4096 == BN * ROW_B, "tile split into 1 KiB wave loads");
+    constexpr int NC = D / (2 * KPL);      // MFMA steps along D (Sᵀ)
+    constexpr int NBLK = BN / 32;          // 32-key blocks per tile
+    constexpr int NKC = BN / (2 * KPL);    // MFMA steps along keys (Oᵀ)
+    constexpr int NDB = D / 32;            // 32-dim blocks of O
 
-    __shared__ __attribute__((aligned(16))) T smem[2 * 2 * KT];  // [buf][K|V][BN][KSTR]
+    // Two tile buffers, each [K | V], each row-major [BN][D] with swizzled slots.
+    __shared__ __attribute__((aligned(1024))) T lds[2][2 * TILE_E];
+    T* const lds0 = lds[0];
+    T* const lds1 = lds[1];
 
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
     // head) are split into 8 contiguous ranges, one per XCD, so the query
-    // heads sharing a K/V head share that XCD's L2; within an XCD the query
-    // blocks run heaviest first under causal masking.
+    // heads sharing a K/V head share that XCD's L2.  Under causal masking the
+    // query blocks are ordered heaviest first for the first half of the
+    // launch and lightest first for the second half, so the two workgroups
+    // that the dispatcher co-schedules on a CU (i and i + grid/2) carry equal
+    // total work when the whole grid is resident at once.
     const int wg = blockIdx.x;
     int unit, qb_rank;
     if (p.xcd_chunk > 0) {
@@ -194,7 +224,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
         qb_rank = wg / p.n_units;
         unit = wg % p.n_units;
     }
-    const int qb = CAUSAL ? (p.n_qb - 1 - qb_rank) : qb_rank;
+    int qb = qb_rank;
+    if (CAUSAL) {
+        const int half = (p.n_qb + 1) >> 1;
+        qb = qb_rank < half ? p.n_qb - 1 - qb_rank : qb_rank - half;
+    }
     const int jg = unit % p.group;
     const int bg = unit / p.group;
     const int g = bg % p.Hkv;
@@ -238,41 +272,53 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     if (CAUSAL) key_end = key_end < q0 + BM ? key_end : q0 + BM;
     const int n_tiles = (key_end + BN - 1) / BN;
 
-    // ---- tile staging: global -> registers -> LDS -------------------------
-    // Buffer loads address the (batch, kv head) slice; rows at or past S fall
-    // outside the resource and read as zero.  Per-thread offsets are fixed;
-    // the tile position is a scalar offset.
-    const uint32_t kv_bytes = uint32_t((int64_t(S) * kvstride - int64_t(g) * D) * int64_t(sizeof(T)));
+    // ---- tile loads: global -> LDS directly -------------------------------
+    // Buffer resources cover this (batch, kv head) slice; rows at or past S
+    // read as zero.  Wave w fills bytes [w·NLD KiB, (w+1)·NLD KiB) of each
+    // tile; lane l writes the 16-byte slot at l·16 of its KiB, i.e. row
+    // (KiB offset + 16 l) / ROW_B at physical slot p, which holds logical
+    // slot p ^ swz(row) of that key row.
+    const uint32_t kv_bytes = uint32_t((int64_t(S) * kvstride - int64_t(g) * D) * int64_t(ES));
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kv_bytes);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, kv_bytes);
-    const uint32_t row_bytes = uint32_t(kvstride * int64_t(sizeof(T)));
-    uint32_t koff[NK];
+    const uint32_t row_bytes = uint32_t(kvstride * int64_t(ES));
+    uint32_t ld_off[NLD];
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-        const int c = tid + kThreads * i;
-        koff[i] = uint32_t(c / (D / CH)) * row_bytes + uint32_t((c % (D / CH)) * CH * int(sizeof(T)));
+    for (int i = 0; i < NLD; ++i) {
+        const int byte = (wave * NLD + i) * 1024 + lane * 16;
+        const int row = byte / ROW_B;
+        const int lslot = ((byte % ROW_B) / 16) ^ swz<NS>(row);
+        ld_off[i] = uint32_t(row) * row_bytes + uint32_t(lslot * 16);
     }
-    u32x4 kreg[NK];
-    u32x4 vreg[NK];
-    auto load_tile = [&](int kb) {
-        const uint32_t soff = uint32_t(kb) * row_bytes;
+    auto issue_tile = [&](T* dst, int kb) {
+        const uint32_t tile_off = uint32_t(kb) * row_bytes;
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            kreg[i] = buf_load16(krs, koff[i], soff);
-            vreg[i] = buf_load16(vrs, koff[i], soff);
+        for (int i = 0; i < NLD; ++i) {
+            T* d = dst + ((wave * NLD + i) * 1024) / ES;
+            lds_dma16(krs, d, ld_off[i] + tile_off);
+            lds_dma16(vrs, d + TILE_E, ld_off[i] + tile_off);
         }
     };
-    auto store_tile = [&](int buf) {
-        T* ks = smem + buf * (2 * KT);
-        T* vs = ks + KT;
+
+    // ---- per-lane LDS read offsets (elements, within a tile) ---------------
+    const int prow = perm_row(r);
+    const int xk = swz<NS>(prow);  // swizzle of every K row this lane reads (row ≡ prow mod 16)
+    // transposing V reads: lane addresses key (r & 15) >> 2 of a 4-key group,
+    // head dims 16·(r >> 4) + 4·swap01(r & 3) .. +3 of each 32-dim block
+    const int tr_key = (r & 15) >> 2;
+    const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
+    // element offset of this lane's transposing read for (db, h) at kc = 0;
+    // key 16·kc + k has the swizzle of k (16·kc ≡ 0 mod 16), so kc only adds
+    // the constant 16·kc·D
+    int v_off[NDB][2];
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int c = tid + kThreads * i;
-            const int off = (c / (D / CH)) * KSTR + (c % (D / CH)) * CH;
-            *reinterpret_cast<u32x4*>(ks + off) = kreg[i];
-            *reinterpret_cast<u32x4*>(vs + off) = vreg[i];
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key = 8 * gl + 4 * h + tr_key;
+            const int col = 32 * db + tr_col;
+            v_off[db][h] = key * D + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH;
         }
-    };
 
     // ---- online-softmax state ----------------------------------------------
     f32x16 oacc[NDB];
@@ -282,116 +328,117 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     float l_run = 0.0f;       // running sum of the rounded P (this lane's half of the keys)
     float l_lse = 0.0f;       // running sum of the unrounded P, for the LSE output
     const float sl2 = p.sl2;
-    const int prow = perm_row(r);
-    // Transposing-read address of this lane inside a 4-key × 32-dim block:
-    // row (r & 15) >> 2, columns 16·(r >> 4) + 4·swap01(r & 3) (see lds_read_tr16).
-    const int tr_off = ((r & 15) >> 2) * KSTR + 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
 
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
+    auto compute_tile = [&](const T* ks, int kb) {
+        const T* vs = ks + TILE_E;
+        // Sᵀ = K · Qᵀ for this wave's 32 rows
+        f32x16 sacc[NBLK];
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) sacc[blk] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * 2 * KPL + gl * KPL;
+            const int off = (((col / CH) ^ xk) * CH) + col % CH;
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk) {
+                const op_t a = load_op<op_t>(ks + (prow + 32 * blk) * D + off);
+                sacc[blk] = mfma(a, qv[c], sacc[blk]);
+            }
+        }
+        // mask: keys past the valid length, and keys after the row (causal)
+        const bool need_mask = (kb + BN > key_lim) || (CAUSAL && kb + BN - 1 > wrow0);
+        if (need_mask) {
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = kb + kidx(16 * blk + i, gl);
+                    const bool ok = key < key_lim && (!CAUSAL || key <= qrow);
+                    if (!ok) sacc[blk][i] = -INFINITY;
+                }
+        }
+        // online softmax
+        float mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+        mx = max_xor32(mx) * sl2;
+        // raise the running max only when some row of the wave needs it
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+            if constexpr (LSE) l_lse *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+        float rs = 0.0f;
+        float rs_lse = 0.0f;
+        op_t pb[NKC];
+#pragma unroll
+        for (int f = 0; f < 16 * NBLK; ++f) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[f >> 4][f & 15], sl2, -m_use));
+            if constexpr (KPL == 1) {
+                pb[f] = pv;
+                rs += pv;
+            } else {
+                pb[f / KPL][f % KPL] = to_t<T>(pv);
+                if constexpr (LSE) rs_lse += pv;
+            }
+        }
+        if constexpr (KPL == 1) {
+            rs_lse = rs;
+        } else {
+            typedef T t2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+                for (int e = 0; e < KPL; e += 2) rs = sum2(t2{pb[kc][e], pb[kc][e + 1]}, rs);
+        }
+        l_run += rs;
+        if constexpr (LSE) l_lse += rs_lse;
+        // Oᵀ += Vᵀ · Pᵀ
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                op_t a;
+                if constexpr (KPL == 1) {
+                    const int key = kidx(kc, gl);
+                    const int col = 32 * db + prow;
+                    a = vs[key * D + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH];
+                } else {
+                    s16x4 half[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) half[h] = lds_read_tr16(vs + 16 * kc * D + v_off[db][h]);
+                    a = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+                oacc[db] = mfma(a, pb[kc], oacc[db]);
+            }
+        }
+    };
+
+    // ---- main loop: two LDS buffers, tile j+1 loads while tile j computes ---
+    if (n_tiles > 0) issue_tile(lds0, 0);
     // All loads issued so far (Q and the first tile) are complete here on
     // every path; saying so keeps the loop free of waits on them.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-
-    for (int j = 0; j < n_tiles; ++j) {
+    for (int j = 0; j < n_tiles; j += 2) {
         const int kb = j * BN;
-        const bool more = j + 1 < n_tiles;
-        if (more) load_tile(kb + BN);
-
-        const T* ks = smem + (j & 1) * (2 * KT);
-        const T* vs = ks + KT;
-        const bool active = !CAUSAL || kb <= wrow0 + 31;
-        if (active) {
-            // Sᵀ = K · Qᵀ for this wave's 32 rows
-            f32x16 sacc[NBLK];
-#pragma unroll
-            for (int blk = 0; blk < NBLK; ++blk) sacc[blk] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-#pragma unroll
-                for (int blk = 0; blk < NBLK; ++blk) {
-                    const op_t a = load_op<op_t>(ks + (prow + 32 * blk) * KSTR + c * 2 * KPL + gl * KPL);
-                    sacc[blk] = mfma(a, qv[c], sacc[blk]);
-                }
-            }
-            // mask: keys past the valid length, and keys after the row (causal)
-            const bool need_mask = (kb + BN > key_lim) || (CAUSAL && kb + BN - 1 > wrow0);
-            if (need_mask) {
-#pragma unroll
-                for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kb + kidx(16 * blk + i, gl);
-                        const bool ok = key < key_lim && (!CAUSAL || key <= qrow);
-                        if (!ok) sacc[blk][i] = -INFINITY;
-                    }
-            }
-            // online softmax
-            float mx = -INFINITY;
-#pragma unroll
-            for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-            mx = max_xor32(mx) * sl2;
-            // raise the running max only when some row of the wave needs it
-            if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
-                if constexpr (LSE) l_lse *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-                m_run = m_new;
-            }
-            const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-            float rs = 0.0f;
-            float rs_lse = 0.0f;
-            op_t pb[NKC];
-#pragma unroll
-            for (int f = 0; f < 16 * NBLK; ++f) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[f >> 4][f & 15], sl2, -m_use));
-                if constexpr (KPL == 1) {
-                    pb[f] = pv;
-                    rs += pv;
-                } else {
-                    pb[f / KPL][f % KPL] = to_t<T>(pv);
-                    if constexpr (LSE) rs_lse += pv;
-                }
-            }
-            if constexpr (KPL == 1) rs_lse = rs;
-            if constexpr (KPL != 1) {
-                typedef T t2 __attribute__((ext_vector_type(2)));
-#pragma unroll
-                for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-                    for (int e = 0; e < KPL; e += 2)
-                        rs = sum2(t2{pb[kc][e], pb[kc][e + 1]}, rs);
-            }
-            l_run += rs;
-            if constexpr (LSE) l_lse += rs_lse;
-            // Oᵀ += Vᵀ · Pᵀ
-#pragma unroll
-            for (int kc = 0; kc < NKC; ++kc) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    op_t a;
-                    if constexpr (KPL == 1) {
-                        a = vs[kidx(kc, gl) * KSTR + 32 * db + prow];
-                    } else {
-                        const T* src = vs + (16 * kc + 8 * gl) * KSTR + 32 * db + tr_off;
-                        const s16x4 lo = lds_read_tr16(src);
-                        const s16x4 hi = lds_read_tr16(src + 4 * KSTR);
-                        a = __builtin_bit_cast(op_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    }
-                    oacc[db] = mfma(a, pb[kc], oacc[db]);
-                }
-            }
-        }
-
-        if (more) store_tile((j + 1) & 1);
+        const bool wave_live0 = !CAUSAL || kb <= wrow0 + 31;
+        if (j + 1 < n_tiles) issue_tile(lds1, kb + BN);
+        if (wave_live0) compute_tile(lds0, kb);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads into lds1 landed
+        __syncthreads();
+        if (j + 1 >= n_tiles) break;
+        const bool wave_live1 = !CAUSAL || kb + BN <= wrow0 + 31;
+        if (j + 2 < n_tiles) issue_tile(lds0, kb + 2 * BN);
+        if (wave_live1) compute_tile(lds1, kb + BN);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
 
