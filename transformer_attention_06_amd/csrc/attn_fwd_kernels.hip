@@ -201,10 +201,14 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
     constexpr int NKC = BN / (2 * KPL);    // MFMA steps along keys (Oᵀ)
     constexpr int NDB = D / 32;            // 32-dim blocks of O
 
-    // Two tile buffers, each [K | V], each row-major [BN][D] with swizzled slots.
-    __shared__ __attribute__((aligned(1024))) T lds[2][2 * TILE_E];
-    T* const lds0 = lds[0];
-    T* const lds1 = lds[1];
+    // K and V tiles, each double-buffered, each row-major [BN][D] with
+    // swizzled slots.  Four distinct objects: the compiler can then see that
+    // a tile being read never aliases the tiles whose loads are in flight,
+    // and does not wait for those loads before the reads.
+    __shared__ __attribute__((aligned(1024))) T kbuf0[TILE_E];
+    __shared__ __attribute__((aligned(1024))) T kbuf1[TILE_E];
+    __shared__ __attribute__((aligned(1024))) T vbuf0[TILE_E];
+    __shared__ __attribute__((aligned(1024))) T vbuf1[TILE_E];
 
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
@@ -290,14 +294,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
         const int lslot = ((byte % ROW_B) / 16) ^ swz<NS>(row);
         ld_off[i] = uint32_t(row) * row_bytes + uint32_t(lslot * 16);
     }
-    auto issue_tile = [&](T* dst, int kb) {
+    auto issue = [&](__amdgpu_buffer_rsrc_t rs, T* dst, int kb) {
         const uint32_t tile_off = uint32_t(kb) * row_bytes;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            T* d = dst + ((wave * NLD + i) * 1024) / ES;
-            lds_dma16(krs, d, ld_off[i] + tile_off);
-            lds_dma16(vrs, d + TILE_E, ld_off[i] + tile_off);
-        }
+        for (int i = 0; i < NLD; ++i) lds_dma16(rs, dst + ((wave * NLD + i) * 1024) / ES, ld_off[i] + tile_off);
     };
 
     // ---- per-lane LDS read offsets (elements, within a tile) ---------------
@@ -329,10 +329,8 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
     float l_lse = 0.0f;       // running sum of the unrounded P, for the LSE output
     const float sl2 = p.sl2;
 
-    auto compute_tile = [&](const T* ks, int kb) {
-        const T* vs = ks + TILE_E;
-        // Sᵀ = K · Qᵀ for this wave's 32 rows
-        f32x16 sacc[NBLK];
+    // Sᵀ = K · Qᵀ for this wave's 32 rows, K from an LDS tile
+    auto gemm1 = [&](const T* ks, f32x16 (&sacc)[NBLK]) {
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk) sacc[blk] = f32x16{};
 #pragma unroll
@@ -345,6 +343,10 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
                 sacc[blk] = mfma(a, qv[c], sacc[blk]);
             }
         }
+    };
+
+    // Mask, running max and (rare) rescale for the scores of the tile at kb.
+    auto softmax_max = [&](f32x16 (&sacc)[NBLK], int kb) {
         // mask: keys past the valid length, and keys after the row (causal)
         const bool need_mask = (kb + BN > key_lim) || (CAUSAL && kb + BN - 1 > wrow0);
         if (need_mask) {
@@ -357,12 +359,13 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
                     if (!ok) sacc[blk][i] = -INFINITY;
                 }
         }
-        // online softmax
-        float mx = -INFINITY;
+        // row max over this lane's 16·NBLK scores in four independent chains
+        float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
         for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+            for (int i = 0; i < 16; ++i) mp[i & 3] = fmaxf(mp[i & 3], sacc[blk][i]);
+        float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
         mx = max_xor32(mx) * sl2;
         // raise the running max only when some row of the wave needs it
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
@@ -374,33 +377,42 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
             for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
             m_run = m_new;
         }
+    };
+
+    // Exponentials, P packed into MFMA operands, row sums.
+    auto softmax_exp = [&](const f32x16 (&sacc)[NBLK], op_t (&pb)[NKC]) {
         const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-        float rs = 0.0f;
-        float rs_lse = 0.0f;
-        op_t pb[NKC];
+        // row sums in four independent chains
+        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float rl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int f = 0; f < 16 * NBLK; ++f) {
             const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[f >> 4][f & 15], sl2, -m_use));
             if constexpr (KPL == 1) {
                 pb[f] = pv;
-                rs += pv;
+                rs[f & 3] += pv;
             } else {
                 pb[f / KPL][f % KPL] = to_t<T>(pv);
-                if constexpr (LSE) rs_lse += pv;
+                if constexpr (LSE) rl[f & 3] += pv;
             }
         }
         if constexpr (KPL == 1) {
-            rs_lse = rs;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rl[i] = rs[i];
         } else {
             typedef T t2 __attribute__((ext_vector_type(2)));
 #pragma unroll
             for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-                for (int e = 0; e < KPL; e += 2) rs = sum2(t2{pb[kc][e], pb[kc][e + 1]}, rs);
+                for (int e = 0; e < KPL; e += 2)
+                    rs[(kc * KPL + e) / 2 & 3] = sum2(t2{pb[kc][e], pb[kc][e + 1]}, rs[(kc * KPL + e) / 2 & 3]);
         }
-        l_run += rs;
-        if constexpr (LSE) l_lse += rs_lse;
-        // Oᵀ += Vᵀ · Pᵀ
+        l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        if constexpr (LSE) l_lse += (rl[0] + rl[1]) + (rl[2] + rl[3]);
+    };
+
+    // Oᵀ += Vᵀ · Pᵀ, V from an LDS tile
+    auto gemm2 = [&](const T* vs, const op_t (&pb)[NKC]) {
 #pragma unroll
         for (int kc = 0; kc < NKC; ++kc) {
 #pragma unroll
@@ -421,23 +433,45 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
         }
     };
 
-    // ---- main loop: two LDS buffers, tile j+1 loads while tile j computes ---
-    if (n_tiles > 0) issue_tile(lds0, 0);
+    // One tile: Sᵀ from K, softmax, O += P·V from V.  (A variant that
+    // overlapped the next tile's Sᵀ with this tile's softmax needed a second
+    // score tile in registers and ran slower at two wavefronts per SIMD.)
+    auto step = [&](int kb, const T* ks, const T* vs) {
+        if (CAUSAL && kb > wrow0 + 31) return;  // no key of the tile is visible to this wave
+        f32x16 sacc[NBLK];
+        gemm1(ks, sacc);
+        softmax_max(sacc, kb);
+        op_t pb[NKC];
+        softmax_exp(sacc, pb);
+        gemm2(vs, pb);
+    };
+
+    // ---- main loop ----------------------------------------------------------
+    // Tile j computes from buffer j % 2 while tile j+1 loads into the other;
+    // one barrier per tile publishes the loads and releases the buffer.
+    if (n_tiles > 0) {
+        issue(krs, kbuf0, 0);
+        issue(vrs, vbuf0, 0);
+    }
     // All loads issued so far (Q and the first tile) are complete here on
     // every path; saying so keeps the loop free of waits on them.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     for (int j = 0; j < n_tiles; j += 2) {
         const int kb = j * BN;
-        const bool wave_live0 = !CAUSAL || kb <= wrow0 + 31;
-        if (j + 1 < n_tiles) issue_tile(lds1, kb + BN);
-        if (wave_live0) compute_tile(lds0, kb);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads into lds1 landed
+        if (j + 1 < n_tiles) {
+            issue(krs, kbuf1, kb + BN);
+            issue(vrs, vbuf1, kb + BN);
+        }
+        step(kb, kbuf0, vbuf0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads landed
         __syncthreads();
         if (j + 1 >= n_tiles) break;
-        const bool wave_live1 = !CAUSAL || kb + BN <= wrow0 + 31;
-        if (j + 2 < n_tiles) issue_tile(lds0, kb + 2 * BN);
-        if (wave_live1) compute_tile(lds1, kb + BN);
+        if (j + 2 < n_tiles) {
+            issue(krs, kbuf0, kb + 2 * BN);
+            issue(vrs, vbuf0, kb + 2 * BN);
+        }
+        step(kb + BN, kbuf1, vbuf1);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     }
