@@ -1,16 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the fused attention forward on one MI355X.
 
-A step is one attn_fwd call over one batch of seeded synthetic input of the
+A step is one attn_fwd call (one kernel launch) over one batch of seeded synthetic input of the
 Llama-2-7B-shaped causal prefill (B=1, H=32, S=2048, D=128, bf16) with inputs
 already resident in device memory.  Throughput counts 4·B·H·S²·D FLOPs,
-halved under causal masking, over the wall time of K timed steps; the
+halved under causal masking, over the wall time of K timed steps (captured
+once as a HIP graph and replayed; --no-graph times eager launches); the
 roofline block divides the same FLOP count by the kernel's average duration
-measured with HIP events on the launch stream.  The cpu_baseline block times
-the fp64 CPU oracle on a bounded sample of heads of the same workload.
+over the same back-to-back launches, measured with HIP events on the launch
+stream.  roofline.traffic is the measured device-memory traffic per launch
+(FETCH_SIZE + WRITE_SIZE counters scaled by a plain copy of known size), read
+from profiles/traffic_<workload>.json when that file was taken on the current
+kernel source, else null.  The cpu_baseline block times the fp64 CPU oracle on
+a bounded sample of heads of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--all]
+                    [--no-cpu-baseline] [--all] [--copy-calibration]
 """
 
 import argparse
@@ -45,7 +50,7 @@ def min_hbm_bytes(w, pad):
     return qo + kv + lse
 
 
-def run_gpu(w, steps, warmup):
+def run_gpu(w, steps, warmup, use_graph=True):
     import torch
     from transformer_attention_06_amd import attn as A
     from transformer_attention_06_amd import workloads as W
@@ -60,30 +65,87 @@ def run_gpu(w, steps, warmup):
     out = torch.empty_like(qd)
     lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda") if w.want_lse else None
     mask = A.ATTN_MASK_NONE if pad is None else A.ATTN_MASK_KEY_PADDING
-    stream = torch.cuda.current_stream()
-
     def step():
-        A.attn_fwd(qd, kd, vd, mask, pad_d, None, w.causal, w.Hq, w.Hkv, out, lse, stream)
+        # launches on the current stream (the capture stream while capturing)
+        A.attn_fwd(qd, kd, vd, mask, pad_d, None, w.causal, w.Hq, w.Hkv, out, lse)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    # HIP events on the launch stream bracket every launch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    graph = None
+    if use_graph:
+        # The K timed steps are captured once as a HIP graph and replayed, so
+        # the device runs them back to back without host launch gaps.
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                step()
+        graph.replay()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    # Timed region: K steps on the launch stream, bracketed by HIP events on
+    # that stream (device time per launch) and by synchronize + a host clock
+    # (wall time, the reported throughput).
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
+    e0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(steps):
+            step()
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    return dict(ms_per_step=(t1 - t0) * 1e3 / steps, kernel_ms_mean=float(kern_ms.mean()),
-                kernel_ms_median=float(np.median(kern_ms)), kernel_ms_min=float(kern_ms.min()),
-                pad=pad)
+    dev_ms = e0.elapsed_time(e1)
+    return dict(ms_per_step=(t1 - t0) * 1e3 / steps, kernel_ms_mean=dev_ms / steps, pad=pad)
+
+
+KERNEL_SOURCES = ["transformer_attention_06_amd/csrc/attn_fwd_kernels.hip",
+                  "transformer_attention_06_amd/csrc/attn_api.cpp"]
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """Bytes per launch from a committed counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(nbytes=1 << 29, reps=3):
+    """A plain device-to-device copy of known size, for scaling the memory
+    traffic counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
+                      "kernel_source_sha": kernel_source_sha()}), flush=True)
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -119,10 +181,10 @@ def cpu_baseline(w, budget_s=12.0):
                       f"full SxS score matrix, {el:.2f} s wall"}
 
 
-def bench_one(name, steps, warmup, with_cpu):
+def bench_one(name, steps, warmup, with_cpu, use_graph=True):
     from transformer_attention_06_amd import workloads as W
     w = W.WORKLOADS[name]
-    r = run_gpu(w, steps, warmup)
+    r = run_gpu(w, steps, warmup, use_graph)
     fl = metric_flops(w)
     value = fl / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = fl / (r["kernel_ms_mean"] * 1e-3) / 1e12
@@ -142,11 +204,12 @@ def bench_one(name, steps, warmup, with_cpu):
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape; no weights)",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "causal": w.causal, "mask": "key_padding" if w.mask_kind else "none",
-                   "lse": w.want_lse, "pct_of_peak_wall": round(100 * value / peak, 2)},
+                   "lse": w.want_lse, "timing": "hip_graph_replay" if use_graph else "eager_launches",
+                   "pct_of_peak_wall": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(w.name),
                      "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 3),
-                     "kernel_us_median": round(r["kernel_ms_median"] * 1e3, 3),
                      "flops_per_launch": fl,
                      "min_hbm_bytes_per_launch": min_hbm_bytes(w, r["pad"])},
     }
@@ -163,6 +226,10 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU leg)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of a replayed HIP graph of the K steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 512 MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -172,13 +239,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (MI355X).", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.all:
         from transformer_attention_06_amd import workloads as W
         for name in W.WORKLOADS:
-            print(json.dumps(bench_one(name, args.steps, args.warmup, False)), flush=True)
+            print(json.dumps(bench_one(name, args.steps, args.warmup, False, not args.no_graph)), flush=True)
         return
-    print(json.dumps(bench_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline)),
-          flush=True)
+    print(json.dumps(bench_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline,
+                               not args.no_graph)), flush=True)
 
 
 if __name__ == "__main__":

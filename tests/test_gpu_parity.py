@@ -280,3 +280,31 @@ def test_noncontiguous_rejected():
     x = torch.zeros(1, 64, 2, 128, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         A.flash_attention(x.transpose(1, 2), x.transpose(1, 2), x.transpose(1, 2))
+
+
+def test_graph_replay_matches_eager():
+    """A captured launch replayed several times, with eager work and
+    synchronisations in between, reproduces the eager result every time."""
+    q, k, v = W.random_inputs(25, 1, 333, 4, 2, 128)
+    qd, _ = prep(q, "bf16")
+    kd, _ = prep(k, "bf16")
+    vd, _ = prep(v, "bf16")
+    ref_o, ref_l = run(qd, kd, vd, causal=True)
+    out = torch.empty_like(qd)
+    lse = torch.empty((1, 4, 333), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        A.attn_fwd(qd, kd, vd, 0, None, None, True, 4, 2, out, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.attn_fwd(qd, kd, vd, 0, None, None, True, 4, 2, out, lse)
+    for i in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+        run(qd, kd, vd, causal=False)  # eager work between replays
