@@ -7,6 +7,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -29,20 +30,43 @@ def hipcc():
 
 
 def build(verbose=False, extra_flags=()):
-    """Compile every source into LIB; returns the library path."""
+    """Compile every source into LIB; returns the library path.  The device
+    assembly of the kernels is compiled alongside and checked for MFMA wait
+    states (asm_check); the library is only installed if that check passes."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}", *DEVICE_FLAGS,
-           *extra_flags, "-o", tmp]
+    common = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
+              *DEVICE_FLAGS, *extra_flags]
+    cmd = [hipcc(), *common, "-shared", "-Wall", "-Wno-unused-result", "-Wno-pass-failed", "-o", tmp]
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and (res.stdout or res.stderr):
-        sys.stderr.write(res.stdout + res.stderr)
+    with tempfile.TemporaryDirectory() as td:
+        asm = os.path.join(td, "kernels.s")
+        acmd = [hipcc(), *common, "--cuda-device-only", "-S", "-o", asm,
+                os.path.join(CSRC, "attn_fwd_kernels.hip")]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+            print(" ".join(acmd), flush=True)
+        lib_p = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        asm_p = subprocess.Popen(acmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        out, err = lib_p.communicate()
+        aout, aerr = asm_p.communicate()
+        if lib_p.returncode != 0:
+            sys.stderr.write(out + err)
+            raise RuntimeError(f"hipcc failed with exit code {lib_p.returncode}")
+        if asm_p.returncode != 0:
+            sys.stderr.write(aout + aerr)
+            raise RuntimeError(f"hipcc (device assembly) failed with exit code {asm_p.returncode}")
+        if verbose and (out or err):
+            sys.stderr.write(out + err)
+        sys.path.insert(0, PKG)
+        try:
+            import asm_check
+        finally:
+            sys.path.pop(0)
+        with open(asm) as f:
+            problems = asm_check.check_asm(f.read())
+    if problems:
+        os.remove(tmp)
+        raise RuntimeError("MFMA wait-state check failed:\n" + "\n".join(problems[:20]))
     os.replace(tmp, LIB)
     return LIB
 

@@ -34,6 +34,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn_fwd.h"
 #include "attn_launch.h"
@@ -80,19 +81,40 @@ __device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// The same products as ordered inline assembly: the tile loop issues its
+// MFMAs, operand reads and VALU work in a fixed interleaved order, and
+// assembly statements are never reordered against each other or against
+// memory operations.  "+v" accumulates in place; the zero-start form writes a
+// fresh accumulator (early-clobber: no overlap with the operands).
+__device__ __forceinline__ void mfma_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc(f32x16& c, const f16x8& a, const f16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// fp32 (a parity path, at the register limit at D = 128): the compiler's
+// own MFMA, so that its hazard tracking covers any copy it inserts
+__device__ __forceinline__ void mfma_acc(f32x16& c, const float& a, const float& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_zero(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_zero(f32x16& c, const f16x8& a, const f16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_zero(f32x16& c, const float& a, const float& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, f32x16{}, 0, 0, 0);
+}
+// Empty assembly statements that fix where VALU work happens in the stream:
+// keep() marks values as needed at this point (computed no later); touch()
+// marks a value as redefined here (work using it starts no earlier).
+__device__ __forceinline__ void keep(float x) { asm volatile("" : : "v"(x)); }
+__device__ __forceinline__ void touch(float& x) { asm volatile("" : "+v"(x)); }
+
 template <typename OP, typename T>
 __device__ __forceinline__ OP load_op(const T* p) {
     return *reinterpret_cast<const OP*>(p);
-}
-
-// Buffer resource over [base, base + bytes): loads at offsets at or past the
-// end return zero, which zero-fills K/V rows beyond the sequence end without
-// branches.  Word 3 is the gfx9-family default data format.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), 0);
 }
 
 // Combine a value with the one held by lane l^32 (the other half of the
@@ -174,17 +196,50 @@ __device__ __forceinline__ int swz(int row) {
         return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-template <typename T>
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, T* lds_dst, uint32_t voff) {
-    // one 16-byte global load per lane, written to lds_dst + 16 * lane
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_dst), 16,
-                                             voff, 0, 0, 0);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource words for [base, base + bytes) (gfx9 default data format);
+// loads at offsets at or past the end return zero.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xffff), int(bytes), 0x00020000};
 }
 
-// 16-bit instances keep two wavefronts per SIMD (two workgroups per CU); the
-// fp32 instances hold twice the operand registers and run one.
+// One 16-byte global load per lane, written to LDS at lds_byte + 16·lane
+// (buffer_load_dwordx4 with LDS destination; M0 holds the LDS address).
+// Issued as inline assembly on purpose: the compiler then does not track
+// these LDS writes and inserts no waits for them before unrelated LDS reads
+// (it cannot prove the tile being read differs from the tile being loaded).
+// Every read of a loaded tile is ordered explicitly instead: the loading
+// wave waits vmcnt(0), then a workgroup barrier.  No other code in the kernel
+// uses M0.
+__device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t lds_byte, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_byte), "v"(voff), "s"(rs)
+                 : "memory");
+}
+
+// Work of one workgroup: one (batch, query head, 128-row query block); four
+// wavefronts of 32 rows each.  Two workgroups share a CU (two wavefronts per
+// SIMD), so the stalls of one wavefront's stream are filled by the other's.
+// Under causal masking the first half of the launch takes the blocks
+// heaviest first and the second half lightest first, so the workgroups that
+// end up sharing a CU even out.
+//
+// Each wavefront software-pipelines its own tile loop.  Step j (key tile j)
+// is one fixed instruction stream of two parts:
+//   A: the MFMAs of Sᵀ(j+1) = K(j+1)·Qᵀ, interleaved with the running-max
+//      update and the first half of the exponentials of S(j);
+//   B: the MFMAs of Oᵀ += Vᵀ(j)·Pᵀ(j), interleaved with the remaining
+//      exponentials, packing P(j) into MFMA operands, the row sums, and the
+//      mask and row maxima of S(j+1).
+// MFMA operands are read from LDS PF products ahead of their use.  K and V
+// tiles are double-buffered in LDS; step j loads K tile j+2 and V tile j+1
+// (one 1 KiB direct load per wavefront every few MFMAs) and ends with a wait
+// for those loads and one workgroup barrier.
 template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
-__global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
     constexpr int KPL = E::KPL;
@@ -200,38 +255,41 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
     constexpr int NBLK = BN / 32;          // 32-key blocks per tile
     constexpr int NKC = BN / (2 * KPL);    // MFMA steps along keys (Oᵀ)
     constexpr int NDB = D / 32;            // 32-dim blocks of O
+    constexpr int NF = 16 * NBLK;          // scores per lane per tile
+    constexpr int NBUF = 2;                // LDS buffers per operand (two workgroups per CU)
+    constexpr int KD = NBUF == 4 ? 3 : 2;  // step t loads K tile t+KD
+    constexpr int VD = NBUF == 4 ? 3 : 1;  // and V tile t+VD
+    constexpr int N1 = NC * NBLK;          // Sᵀ MFMAs per tile
+    constexpr int N2 = NKC * NDB;          // P·V MFMAs per tile
+    constexpr int PF = 6;                  // operand prefetch distance (MFMAs)
+    static_assert(NBUF * TILE_E * ES <= 65536, "buffer offsets fit the LDS immediate");
 
-    // K and V tiles, each double-buffered, each row-major [BN][D] with
-    // swizzled slots.  Four distinct objects: the compiler can then see that
-    // a tile being read never aliases the tiles whose loads are in flight,
-    // and does not wait for those loads before the reads.
-    __shared__ __attribute__((aligned(1024))) T kbuf0[TILE_E];
-    __shared__ __attribute__((aligned(1024))) T kbuf1[TILE_E];
-    __shared__ __attribute__((aligned(1024))) T vbuf0[TILE_E];
-    __shared__ __attribute__((aligned(1024))) T vbuf1[TILE_E];
+    // K tiles [NBUF][BN][D], then V tiles [NBUF][BN][D], slots swizzled.
+    __shared__ __attribute__((aligned(1024))) T lds[2 * NBUF * TILE_E];
+    T* const lds_k = lds;
+    T* const lds_v = lds + NBUF * TILE_E;
 
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
     // head) are split into 8 contiguous ranges, one per XCD, so the query
-    // heads sharing a K/V head share that XCD's L2.  Under causal masking the
-    // query blocks are ordered heaviest first for the first half of the
-    // launch and lightest first for the second half, so the two workgroups
-    // that the dispatcher co-schedules on a CU (i and i + grid/2) carry equal
-    // total work when the whole grid is resident at once.
+    // heads sharing a K/V head share that XCD's L2.
     const int wg = blockIdx.x;
-    int unit, qb_rank;
+    int unit, task;
     if (p.xcd_chunk > 0) {
         const int xcd = wg & 7, local = wg >> 3;
-        qb_rank = local / p.xcd_chunk;
+        task = local / p.xcd_chunk;
         unit = xcd * p.xcd_chunk + local % p.xcd_chunk;
     } else {
-        qb_rank = wg / p.n_units;
+        task = wg / p.n_units;
         unit = wg % p.n_units;
     }
-    int qb = qb_rank;
+    int qb = task;
     if (CAUSAL) {
+        // two workgroups per CU: heaviest first for the first half of the
+        // launch, lightest first for the second half, so the pairs that share
+        // a CU even out
         const int half = (p.n_qb + 1) >> 1;
-        qb = qb_rank < half ? p.n_qb - 1 - qb_rank : qb_rank - half;
+        qb = task < half ? p.n_qb - 1 - task : task - half;
     }
     const int jg = unit % p.group;
     const int bg = unit / p.group;
@@ -240,14 +298,24 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
     const int hq = g * p.group + jg;
 
     const int S = p.S;
+    int key_lim = S;
+    if (PAD) {
+        const int L = p.pad_lens[b];
+        key_lim = L < 0 ? 0 : (L > S ? S : L);
+    }
+    int n = 0;  // key tiles with at least one visible key for this block
+    {
+        int e = key_lim;
+        if (CAUSAL) e = e < qb * BM + BM ? e : qb * BM + BM;
+        n = (e + BN - 1) / BN;
+    }
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wavefront index, made provably uniform so branches on it are scalar
+    const int w4 = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31;
     const int gl = lane >> 5;
-    const int q0 = qb * BM;
-    const int wrow0 = q0 + wave * 32;
-    const int qrow = wrow0 + r;
 
     const int64_t qstride = int64_t(p.Hq) * D;
     const int64_t kvstride = int64_t(p.Hkv) * D;
@@ -255,49 +323,49 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
     const T* kbase = static_cast<const T*>(p.k) + int64_t(b) * p.kv_bstride + int64_t(g) * D;
     const T* vbase = static_cast<const T*>(p.v) + int64_t(b) * p.kv_bstride + int64_t(g) * D;
 
-    // ---- Q tile: MFMA B operands, resident for the whole loop ------------
-    op_t qv[NC];
-    if (qrow < S) {
-        const T* qr = qbase + int64_t(qrow) * qstride;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) qv[c] = load_op<op_t>(qr + c * 2 * KPL + gl * KPL);
-    } else {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) qv[c] = op_t{};
-    }
-
-    // ---- key range ----------------------------------------------------------
-    int key_lim = S;
-    if (PAD) {
-        const int L = p.pad_lens[b];
-        key_lim = L < 0 ? 0 : (L > S ? S : L);
-    }
-    int key_end = key_lim;
-    if (CAUSAL) key_end = key_end < q0 + BM ? key_end : q0 + BM;
-    const int n_tiles = (key_end + BN - 1) / BN;
-
     // ---- tile loads: global -> LDS directly -------------------------------
     // Buffer resources cover this (batch, kv head) slice; rows at or past S
     // read as zero.  Wave w fills bytes [w·NLD KiB, (w+1)·NLD KiB) of each
     // tile; lane l writes the 16-byte slot at l·16 of its KiB, i.e. row
-    // (KiB offset + 16 l) / ROW_B at physical slot p, which holds logical
-    // slot p ^ swz(row) of that key row.
+    // (KiB offset + 16 l) / ROW_B at physical slot p, which holds logical slot
+    // p ^ swz(row) of that key row.  A tile past the last one is "loaded" with
+    // an empty resource (every lane out of range), so every step issues the
+    // same loads and waits on the same count.
     const uint32_t kv_bytes = uint32_t((int64_t(S) * kvstride - int64_t(g) * D) * int64_t(ES));
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, kv_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, kv_bytes);
+    const i32x4 krs = rsrc_words(kbase, kv_bytes);
+    const i32x4 vrs = rsrc_words(vbase, kv_bytes);
+    const i32x4 krs0 = rsrc_words(kbase, 0);
+    const i32x4 vrs0 = rsrc_words(vbase, 0);
     const uint32_t row_bytes = uint32_t(kvstride * int64_t(ES));
-    uint32_t ld_off[NLD];
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-        const int byte = (wave * NLD + i) * 1024 + lane * 16;
-        const int row = byte / ROW_B;
-        const int lslot = ((byte % ROW_B) / 16) ^ swz<NS>(row);
-        ld_off[i] = uint32_t(row) * row_bytes + uint32_t(lslot * 16);
-    }
-    auto issue = [&](__amdgpu_buffer_rsrc_t rs, T* dst, int kb) {
-        const uint32_t tile_off = uint32_t(kb) * row_bytes;
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) lds_dma16(rs, dst + ((wave * NLD + i) * 1024) / ES, ld_off[i] + tile_off);
+    // Load i of a wave covers tile rows rw_i + [0, RPL) with rw_i =
+    // (w·NLD + i)·RPL; lane l takes row rw_i + lr, physical slot ps.  The
+    // swizzle is a bit permutation of the row index and rw_i shares no bits
+    // with lr, so the logical slot is ps ^ swz(lr) ^ swz(rw_i): one per-lane
+    // offset, XORed with a uniform term per load.
+    constexpr int RPL = 1024 / ROW_B;  // tile rows per 1 KiB load
+    const int lr = lane / (ROW_B / 16);
+    const int ps = lane % (ROW_B / 16);
+    const uint32_t ld_base = uint32_t(lr) * row_bytes + uint32_t((ps ^ swz<NS>(lr)) * 16);
+    const uint32_t lds_k_b = uint32_t(reinterpret_cast<uintptr_t>(lds_k));
+    const uint32_t lds_v_b = uint32_t(reinterpret_cast<uintptr_t>(lds_v));
+    // load i (0..2·NLD-1): K tile tk for i < NLD, else V tile tv; buffer
+    // tile % NBUF
+    auto load_one = [&](int tk, int tv, int i) __attribute__((always_inline)) {
+        const bool isv = i >= NLD;
+        const int t = isv ? tv : tk;
+        const int li = isv ? i - NLD : i;
+        const int rw = (w4 * NLD + li) * RPL;
+        uint32_t lb = ld_base;
+        asm volatile("" : "+v"(lb));  // formed here, not hoisted as one register per load
+        const uint32_t voff = (lb ^ uint32_t(swz<NS>(rw) * 16)) + uint32_t(t * BN + rw) * row_bytes;
+        const uint32_t lds_byte = (isv ? lds_v_b : lds_k_b) + uint32_t((t & (NBUF - 1)) * TILE_E * ES) +
+                                  uint32_t((w4 * NLD + li) * 1024);
+        const bool live = t < n;
+        const i32x4 rv = isv ? (live ? vrs : vrs0) : (live ? krs : krs0);
+        // the selection is uniform; keep it in scalar registers
+        const i32x4 rs = {__builtin_amdgcn_readfirstlane(rv[0]), __builtin_amdgcn_readfirstlane(rv[1]),
+                          __builtin_amdgcn_readfirstlane(rv[2]), __builtin_amdgcn_readfirstlane(rv[3])};
+        lds_dma16(rs, __builtin_amdgcn_readfirstlane(lds_byte), voff);
     };
 
     // ---- per-lane LDS read offsets (elements, within a tile) ---------------
@@ -319,191 +387,326 @@ __global__ __launch_bounds__(kThreads, sizeof(T) == 2 ? 2 : 1) void attn_fwd_ker
             const int col = 32 * db + tr_col;
             v_off[db][h] = key * D + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH;
         }
+    const float sl2 = p.sl2;
 
-    // ---- online-softmax state ----------------------------------------------
+    // ---- this wave's 32 rows of the block -----------------------------------
+    const int wrow0 = qb * BM + w4 * 32;
+    const int qrow = wrow0 + r;
+    op_t qv[NC];
+    if (qrow < S) {
+        const T* qr = qbase + int64_t(qrow) * qstride;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qv[c] = load_op<op_t>(qr + c * 2 * KPL + gl * KPL);
+    } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qv[c] = op_t{};
+    }
     f32x16 oacc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;  // running max of scale*log2(e)*score
-    float l_run = 0.0f;       // running sum of the rounded P (this lane's half of the keys)
-    float l_lse = 0.0f;       // running sum of the unrounded P, for the LSE output
-    const float sl2 = p.sl2;
+    float m_run = -INFINITY;  // running max (scaled, log2)
+    float l_run = 0.0f;       // sum of the rounded probabilities
+    float l_lse = 0.0f;       // sum of the exact probabilities (LSE)
 
-    // Sᵀ = K · Qᵀ for this wave's 32 rows, K from an LDS tile
-    auto gemm1 = [&](const T* ks, f32x16 (&sacc)[NBLK]) {
+    // normalise and store O (and LSE) for this wave's rows
+    auto write_rows = [&]() __attribute__((always_inline)) {
+        const float l_tot = sum_xor32(l_run);
+        const float l_e = LSE ? sum_xor32(l_lse) : 0.0f;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        if (qrow < S) {
+            T* orow = static_cast<T*>(p.o) + int64_t(b) * p.q_bstride + int64_t(qrow) * qstride +
+                      int64_t(hq) * D;
 #pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk) sacc[blk] = f32x16{};
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int col = c * 2 * KPL + gl * KPL;
-            const int off = (((col / CH) ^ xk) * CH) + col % CH;
+                for (int h = 0; h < 2; ++h) {
+                    T vals[8];
 #pragma unroll
-            for (int blk = 0; blk < NBLK; ++blk) {
-                const op_t a = load_op<op_t>(ks + (prow + 32 * blk) * D + off);
-                sacc[blk] = mfma(a, qv[c], sacc[blk]);
+                    for (int e = 0; e < 8; ++e) vals[e] = to_t<T>(oacc[db][8 * h + e] * inv);
+                    T* dst = orow + 32 * db + 16 * h + 8 * gl;
+                    if constexpr (sizeof(T) == 2) {
+                        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(vals);
+                    } else {
+                        reinterpret_cast<u32x4*>(dst)[0] = reinterpret_cast<const u32x4*>(vals)[0];
+                        reinterpret_cast<u32x4*>(dst)[1] = reinterpret_cast<const u32x4*>(vals)[1];
+                    }
+                }
+            if (LSE && gl == 0) {
+                const float lse = l_e > 0.0f ? (m_run + __builtin_amdgcn_logf(l_e)) * 0.69314718055994530942f
+                                             : -INFINITY;
+                p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] = lse;
             }
         }
     };
 
-    // Mask, running max and (rare) rescale for the scores of the tile at kb.
-    auto softmax_max = [&](f32x16 (&sacc)[NBLK], int kb) {
-        // mask: keys past the valid length, and keys after the row (causal)
-        const bool need_mask = (kb + BN > key_lim) || (CAUSAL && kb + BN - 1 > wrow0);
-        if (need_mask) {
+    // ---- MFMA operands from LDS ----------------------------------------------
+    // Sᵀ product i (0..N1-1) of a K tile: head-dim step c = i / NBLK, key block
+    // blk = i % NBLK
+    auto fetch_k = [&](const T* ks, int i) __attribute__((always_inline)) -> op_t {
+        const int c = i / NBLK, blk = i % NBLK;
+        const int col = c * 2 * KPL + gl * KPL;
+        const int off = (((col / CH) ^ xk) * CH) + col % CH;
+        return load_op<op_t>(ks + (prow + 32 * blk) * D + off);
+    };
+    // P·V product i (0..N2-1) of a V tile: key step kc = i / NDB, dim block db
+    auto fetch_v = [&](const T* vs, int i) __attribute__((always_inline)) -> op_t {
+        const int kcol = i / NDB, db = i % NDB;
+        if constexpr (KPL == 1) {
+            const int key = kidx(kcol, gl);
+            const int col = 32 * db + prow;
+            return vs[key * D + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH];
+        } else {
+            s16x4 half[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) half[h] = lds_read_tr16(vs + 16 * kcol * D + v_off[db][h]);
+            return __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+
+    // ---- softmax pieces ------------------------------------------------------
+    // keys past the valid length, and keys after the row (causal), score -inf
+    auto mask_tile = [&](f32x16 (&s)[NBLK], int t) __attribute__((always_inline)) {
+        const int kb = t * BN;
+        if ((kb + BN > key_lim) || (CAUSAL && kb + BN - 1 > wrow0)) {
 #pragma unroll
             for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = kb + kidx(16 * blk + i, gl);
                     const bool ok = key < key_lim && (!CAUSAL || key <= qrow);
-                    if (!ok) sacc[blk][i] = -INFINITY;
+                    if (!ok) s[blk][i] = -INFINITY;
                 }
         }
-        // row max over this lane's 16·NBLK scores in four independent chains
-        float mp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-        for (int blk = 0; blk < NBLK; ++blk)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mp[i & 3] = fmaxf(mp[i & 3], sacc[blk][i]);
-        float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-        mx = max_xor32(mx) * sl2;
-        // raise the running max only when some row of the wave needs it
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-            if constexpr (LSE) l_lse *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-            m_run = m_new;
-        }
     };
-
-    // Exponentials, P packed into MFMA operands, row sums.
-    auto softmax_exp = [&](const f32x16 (&sacc)[NBLK], op_t (&pb)[NKC]) {
-        const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
-        // row sums in four independent chains
-        float rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        float rl[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // Softmax work of one tile, split so it can ride along MFMAs:
+    //   max_item(k): partial row maxima over scores 4k..4k+3 (four chains);
+    //   fin0: the row max over both lane halves, scaled to log2 units;
+    //   fin: running-max update (raised only when some row of the wave needs
+    //        it: the exponentials then stay below 2^8 and the output needs no
+    //        rescale), correction factor, scaling of the running sums;
+    //   exp_item(f): the exponential of score f.
+    constexpr int NMX = NF / 4;
+    float mp[4];
+    float mxs = -INFINITY;  // scaled row max of the tile whose maxima were taken last
+    float pf[NF];
+    float alpha = 1.0f, m_use = 0.0f;
+    bool resc = false;
+    auto max_item = [&](const f32x16 (&s)[NBLK], int k) __attribute__((always_inline)) {
+        if (k < 4) mp[k] = -INFINITY;
 #pragma unroll
-        for (int f = 0; f < 16 * NBLK; ++f) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[f >> 4][f & 15], sl2, -m_use));
-            if constexpr (KPL == 1) {
-                pb[f] = pv;
-                rs[f & 3] += pv;
-            } else {
-                pb[f / KPL][f % KPL] = to_t<T>(pv);
-                if constexpr (LSE) rl[f & 3] += pv;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int f = 4 * k + e;
+            mp[k & 3] = fmaxf(mp[k & 3], s[f >> 4][f & 15]);
         }
+        keep(mp[k & 3]);
+    };
+    auto fin0 = [&]() __attribute__((always_inline)) {
+        const float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+        mxs = max_xor32(mx) * sl2;
+        keep(mxs);
+    };
+    auto fin = [&]() __attribute__((always_inline)) {
+        resc = __builtin_amdgcn_ballot_w64(mxs > m_run + kRescaleLog2) != 0;
+        const float m_new = resc ? fmaxf(m_run, mxs) : m_run;
+        alpha = (resc && m_new != -INFINITY) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+        if constexpr (LSE) l_lse *= alpha;
+        m_run = m_new;
+        m_use = m_run == -INFINITY ? 0.0f : m_run;
+        keep(m_use);
+        keep(alpha);
+    };
+    auto exp_item = [&](const f32x16 (&s)[NBLK], int f) __attribute__((always_inline)) {
+        touch(m_use);
+        pf[f] = __builtin_amdgcn_exp2f(fmaf(s[f >> 4][f & 15], sl2, -m_use));
+        keep(pf[f]);
+    };
+    // P operand kc from the exponentials, and its row sums
+    float rs[2] = {0.0f, 0.0f}, rl[2] = {0.0f, 0.0f};
+    auto pack_p = [&](const f32x16 (&s)[NBLK], op_t (&pb)[NKC], int kc) __attribute__((always_inline)) {
         if constexpr (KPL == 1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rl[i] = rs[i];
+            float pv = pf[kc];
+            pb[kc] = pv;
+            rs[kc & 1] += pv;
+            keep(rs[kc & 1]);
+            keep(pb[kc]);
         } else {
+            float x[KPL];
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) {
+                x[e] = pf[kc * KPL + e];
+            }
+#pragma unroll
+            for (int e = 0; e < KPL; ++e) pb[kc][e] = to_t<T>(x[e]);
             typedef T t2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-            for (int kc = 0; kc < NKC; ++kc)
+            for (int e = 0; e < KPL; e += 2) rs[(e >> 1) & 1] = sum2(t2{pb[kc][e], pb[kc][e + 1]}, rs[(e >> 1) & 1]);
+            if constexpr (LSE) {
 #pragma unroll
-                for (int e = 0; e < KPL; e += 2)
-                    rs[(kc * KPL + e) / 2 & 3] = sum2(t2{pb[kc][e], pb[kc][e + 1]}, rs[(kc * KPL + e) / 2 & 3]);
-        }
-        l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        if constexpr (LSE) l_lse += (rl[0] + rl[1]) + (rl[2] + rl[3]);
-    };
-
-    // Oᵀ += Vᵀ · Pᵀ, V from an LDS tile
-    auto gemm2 = [&](const T* vs, const op_t (&pb)[NKC]) {
-#pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                op_t a;
-                if constexpr (KPL == 1) {
-                    const int key = kidx(kc, gl);
-                    const int col = 32 * db + prow;
-                    a = vs[key * D + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH];
-                } else {
-                    s16x4 half[2];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) half[h] = lds_read_tr16(vs + 16 * kc * D + v_off[db][h]);
-                    a = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                }
-                oacc[db] = mfma(a, pb[kc], oacc[db]);
+                for (int e = 0; e < KPL; ++e) rl[e & 1] += x[e];
+                keep(rl[0]);
+                keep(rl[1]);
             }
+            keep(rs[0]);
+            keep(rs[1]);
+            asm volatile("" : : "v"(pb[kc]));  // packed here, before the wait states that follow
+        }
+    };
+    auto finish_sums = [&]() __attribute__((always_inline)) {
+        l_run += rs[0] + rs[1];
+        if constexpr (LSE) l_lse += KPL == 1 ? rs[0] + rs[1] : rl[0] + rl[1];
+        rs[0] = rs[1] = rl[0] = rl[1] = 0.0f;
+    };
+    auto rescale_o = [&]() __attribute__((always_inline)) {
+        if (resc) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
         }
     };
 
-    // One tile: Sᵀ from K, softmax, O += P·V from V.  (A variant that
-    // overlapped the next tile's Sᵀ with this tile's softmax needed a second
-    // score tile in registers and ran slower at two wavefronts per SIMD.)
-    auto step = [&](int kb, const T* ks, const T* vs) {
-        if (CAUSAL && kb > wrow0 + 31) return;  // no key of the tile is visible to this wave
-        f32x16 sacc[NBLK];
-        gemm1(ks, sacc);
-        softmax_max(sacc, kb);
-        op_t pb[NKC];
-        softmax_exp(sacc, pb);
-        gemm2(vs, pb);
+    // ---- one pipelined step --------------------------------------------------
+    // Tile t: S(t) arrives in sc, already masked and with its row maxima
+    // taken (fin0 done); with G1, Sᵀ(t+1) is computed into sn from the K
+    // buffer (t+1) % NBUF.  One operand stream covers both parts: K operands
+    // 0..N1-1, then V operands 0..N2-1, each read PF MFMAs ahead (the first V
+    // operands while part A still runs).
+    //   part A: Sᵀ(t+1) MFMAs; the running-max update, then the exponentials
+    //           of the first NKA P operands; loads of tile t+3;
+    //   part B: P(t)·V(t) MFMAs; the exponentials of the other P operands,
+    //           each finished NDB MFMAs before its first use; the mask and
+    //           row maxima of S(t+1).
+    constexpr int NKA = (NKC + 1) / 2;     // P operands exponentiated in part A
+    constexpr int NEA = NKA * KPL;         // their scores
+    constexpr int MX0 = N2 / 8 > 1 ? N2 / 8 : 1;  // first part-B slot reading S(t+1)
+    op_t pb[NKC];
+    auto step = [&](const int t, const T* kn, const T* vc, f32x16 (&sc)[NBLK], f32x16 (&sn)[NBLK],
+                    const bool G1) __attribute__((always_inline)) {
+        constexpr int NL = 2 * NLD;
+        static_assert(N1 % NL == 0, "loads spread evenly over part A");
+        op_t fr[PF + 1];
+        auto fetch = [&](int g) __attribute__((always_inline)) {
+            fr[g % (PF + 1)] = g < N1 ? fetch_k(kn, g) : fetch_v(vc, g - N1);
+        };
+        const int g0 = G1 ? 0 : N1;  // first operand of this step
+#pragma unroll
+        for (int g = 0; g < PF; ++g)
+            if (g0 + g < N1 + N2) fetch(g0 + g);
+        // part A
+#pragma unroll
+        for (int i = 0; i < N1; ++i) {
+            if (G1) {
+                if (i % (N1 / NL) == 0) load_one(t + KD, t + VD, i / (N1 / NL));
+                if (i + PF < N1 + N2) fetch(i + PF);
+                if (i < NBLK)
+                    mfma_zero(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                else
+                    mfma_acc(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+            }
+            if (i == 0) fin();
+            if (i > 0) {
+#pragma unroll
+                for (int f = (i - 1) * NEA / (N1 - 1); f < i * NEA / (N1 - 1); ++f) exp_item(sc, f);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kc = 0; kc < NKA; ++kc) pack_p(sc, pb, kc);
+        rescale_o();
+        asm volatile("s_nop 4");  // VALU-written operands read by the next MFMA
+        // part B
+#pragma unroll
+        for (int i = 0; i < N2; ++i) {
+            if (N1 + i + PF < N1 + N2) fetch(N1 + i + PF);
+            mfma_acc(oacc[i % NDB], fr[(N1 + i) % (PF + 1)], pb[i / NDB]);
+            // P operand kc (kc >= NKA) is formed over slots [(kc-1)·NDB, kc·NDB)
+            if (i / NDB + 1 >= NKA && i / NDB + 1 < NKC) {
+                const int kc = i / NDB + 1, j = i % NDB;
+#pragma unroll
+                for (int e = j * KPL / NDB; e < (j + 1) * KPL / NDB; ++e) exp_item(sc, kc * KPL + e);
+                if (j == NDB - 1) {
+                    pack_p(sc, pb, kc);
+                    asm volatile("s_nop 1");  // read by the next MFMA
+                }
+            }
+            if (G1) {
+                if (i == MX0) mask_tile(sn, t + 1);
+                if (i >= MX0) {
+#pragma unroll
+                    for (int k = (i - MX0) * NMX / (N2 - MX0); k < (i - MX0 + 1) * NMX / (N2 - MX0); ++k)
+                        max_item(sn, k);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        finish_sums();
+        if (G1) fin0();
+    };
+    // wait for this wave's loads of the previous step, then publish
+    auto end_step = [&]() __attribute__((always_inline)) {
+        static_assert(2 * NLD < 16, "vmcnt immediate");
+        if constexpr (NBUF == 4)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NLD));  // vmcnt(2·NLD): the loads of step t-1 landed
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's loads landed
+        __syncthreads();
     };
 
-    // ---- main loop ----------------------------------------------------------
-    // Tile j computes from buffer j % 2 while tile j+1 loads into the other;
-    // one barrier per tile publishes the loads and releases the buffer.
-    if (n_tiles > 0) {
-        issue(krs, kbuf0, 0);
-        issue(vrs, vbuf0, 0);
-    }
-    // All loads issued so far (Q and the first tile) are complete here on
-    // every path; saying so keeps the loop free of waits on them.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // ---- prologue: K tiles 0..KD-1 and V tiles 0..VD-1 resident, Sᵀ(0) ------
+    f32x16 sa[NBLK], sb[NBLK];
+#pragma unroll
+    for (int t = 0; t < KD; ++t)
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) load_one(t, 0, i);
+#pragma unroll
+    for (int t = 0; t < VD; ++t)
+#pragma unroll
+        for (int i = NLD; i < 2 * NLD; ++i) load_one(0, t, i);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
     __syncthreads();
-    for (int j = 0; j < n_tiles; j += 2) {
-        const int kb = j * BN;
-        if (j + 1 < n_tiles) {
-            issue(krs, kbuf1, kb + BN);
-            issue(vrs, vbuf1, kb + BN);
+    if (n > 0) {
+        op_t fr[PF + 1];
+#pragma unroll
+        for (int f = 0; f < PF; ++f) fr[f] = fetch_k(lds_k, f);
+#pragma unroll
+        for (int i = 0; i < N1; ++i) {
+            if (i + PF < N1) fr[(i + PF) % (PF + 1)] = fetch_k(lds_k, i + PF);
+            if (i < NBLK)
+                mfma_zero(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+            else
+                mfma_acc(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        step(kb, kbuf0, vbuf0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's loads landed
-        __syncthreads();
-        if (j + 1 >= n_tiles) break;
-        if (j + 2 < n_tiles) {
-            issue(krs, kbuf0, kb + 2 * BN);
-            issue(vrs, vbuf0, kb + 2 * BN);
-        }
-        step(kb + BN, kbuf1, vbuf1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-    }
+        // the first softmax reads these accumulators right away: wait out the
+        // MFMA result latency (the products are assembly, so the compiler
+        // does not insert these wait states itself)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+        // step 0 reloads the buffer K tile 0 was read from
+        if constexpr (NBUF == 2) __syncthreads();
+        mask_tile(sa, 0);
+#pragma unroll
+        for (int k = 0; k < NMX; ++k) max_item(sa, k);
+        fin0();
 
-    // ---- epilogue: normalise, store O (and LSE) ---------------------------
-    const float l_tot = sum_xor32(l_run);
-    const float l_e = LSE ? sum_xor32(l_lse) : 0.0f;
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (qrow < S) {
-        T* orow = static_cast<T*>(p.o) + int64_t(b) * p.q_bstride + int64_t(qrow) * qstride +
-                  int64_t(hq) * D;
+        // ---- steps 0 .. n-2 -------------------------------------------------
+        int t = 0;
+        for (; t + 1 < n; ++t) {
+            step(t, lds_k + ((t + 1) & (NBUF - 1)) * TILE_E, lds_v + (t & (NBUF - 1)) * TILE_E, sa, sb, true);
+            end_step();
+            // S(t+1) to the registers step t+1 reads; after the barrier, long
+            // after the MFMAs that wrote it
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                T vals[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vals[e] = to_t<T>(oacc[db][8 * h + e] * inv);
-                T* dst = orow + 32 * db + 16 * h + 8 * gl;
-                if constexpr (sizeof(T) == 2) {
-                    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(vals);
-                } else {
-                    reinterpret_cast<u32x4*>(dst)[0] = reinterpret_cast<const u32x4*>(vals)[0];
-                    reinterpret_cast<u32x4*>(dst)[1] = reinterpret_cast<const u32x4*>(vals)[1];
-                }
+            for (int blk = 0; blk < NBLK; ++blk) {
+                asm volatile("" : "+v"(sb[blk]));
+                sa[blk] = sb[blk];
             }
-        if (LSE && gl == 0) {
-            const float lse = l_e > 0.0f ? (m_run + __builtin_amdgcn_logf(l_e)) * 0.69314718055994530942f
-                                         : -INFINITY;
-            p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] = lse;
         }
+        // ---- last step (t = n-1): no next tile ----------------------------
+        step(t, lds_k, lds_v + (t & (NBUF - 1)) * TILE_E, sa, sb, false);
+        // the output accumulators were last written by MFMAs issued just now
+        // (wait states as after the prologue)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
     }
+    write_rows();
 }
 
 template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
