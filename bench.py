@@ -50,7 +50,7 @@ def min_hbm_bytes(w, pad):
     return qo + kv + lse
 
 
-def run_gpu(w, steps, warmup, use_graph=True):
+def run_gpu(w, steps, warmup, use_graph=True, warmup_s=0.0):
     import torch
     from transformer_attention_06_amd import attn as A
     from transformer_attention_06_amd import workloads as W
@@ -69,8 +69,15 @@ def run_gpu(w, steps, warmup, use_graph=True):
         # launches on the current stream (the capture stream while capturing)
         A.attn_fwd(qd, kd, vd, mask, pad_d, None, w.causal, w.Hq, w.Hkv, out, lse)
 
-    for _ in range(warmup):
+    # Untimed warmup: at least `warmup` steps, and (by default) at least half
+    # a second of them, so the timed region starts at a settled clock.
+    t_w = time.perf_counter()
+    done = 0
+    while done < warmup or (warmup_s > 0 and time.perf_counter() - t_w < warmup_s):
         step()
+        done += 1
+        if done % 20 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     graph = None
@@ -107,7 +114,7 @@ def run_gpu(w, steps, warmup, use_graph=True):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dev_ms = e0.elapsed_time(e1)
-    return dict(ms_per_step=(t1 - t0) * 1e3 / steps, kernel_ms_mean=dev_ms / steps, pad=pad)
+    return dict(ms_per_step=(t1 - t0) * 1e3 / steps, kernel_ms_mean=dev_ms / steps, pad=pad, warmup_done=done)
 
 
 KERNEL_SOURCES = ["transformer_attention_06_amd/csrc/attn_fwd_kernels.hip",
@@ -181,10 +188,10 @@ def cpu_baseline(w, budget_s=12.0):
                       f"full SxS score matrix, {el:.2f} s wall"}
 
 
-def bench_one(name, steps, warmup, with_cpu, use_graph=True):
+def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0):
     from transformer_attention_06_amd import workloads as W
     w = W.WORKLOADS[name]
-    r = run_gpu(w, steps, warmup, use_graph)
+    r = run_gpu(w, steps, warmup, use_graph, warmup_s)
     fl = metric_flops(w)
     value = fl / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = fl / (r["kernel_ms_mean"] * 1e-3) / 1e12
@@ -195,7 +202,7 @@ def bench_one(name, steps, warmup, with_cpu, use_graph=True):
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warmup,
+        "warmup": r["warmup_done"],
         "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -221,8 +228,9 @@ def bench_one(name, steps, warmup, with_cpu, use_graph=True):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: at least 20 steps and 0.5 s)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU leg)")
@@ -231,6 +239,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
+    warmup_s = 0.5 if args.warmup is None else 0.0
+    if args.warmup is None:
+        args.warmup = 20
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
@@ -245,10 +256,10 @@ def main():
     if args.all:
         from transformer_attention_06_amd import workloads as W
         for name in W.WORKLOADS:
-            print(json.dumps(bench_one(name, args.steps, args.warmup, False, not args.no_graph)), flush=True)
+            print(json.dumps(bench_one(name, args.steps, args.warmup, False, not args.no_graph, warmup_s)), flush=True)
         return
     print(json.dumps(bench_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline,
-                               not args.no_graph)), flush=True)
+                               not args.no_graph, warmup_s)), flush=True)
 
 
 if __name__ == "__main__":

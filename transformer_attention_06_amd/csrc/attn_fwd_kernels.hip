@@ -220,6 +220,13 @@ __device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t lds_byte, ui
                  : "memory");
 }
 
+// Wavefront groups per workgroup: two for the 16-bit types (eight wavefronts,
+// two per SIMD), one for fp32 (whose registers do not fit twice per SIMD).
+template <typename T>
+struct Groups {
+    static constexpr int value = sizeof(T) == 2 ? 2 : 1;
+};
+
 // Work of one workgroup: one (batch, query head, 128-row query block); four
 // wavefronts of 32 rows each.  Two workgroups share a CU (two wavefronts per
 // SIMD), so the stalls of one wavefront's stream are filled by the other's.
@@ -239,7 +246,7 @@ __device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t lds_byte, ui
 // (one 1 KiB direct load per wavefront every few MFMAs) and ends with a wait
 // for those loads and one workgroup barrier.
 template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kernel(KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
     constexpr int KPL = E::KPL;
@@ -256,7 +263,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     constexpr int NKC = BN / (2 * KPL);    // MFMA steps along keys (Oᵀ)
     constexpr int NDB = D / 32;            // 32-dim blocks of O
     constexpr int NF = 16 * NBLK;          // scores per lane per tile
-    constexpr int NBUF = 2;                // LDS buffers per operand (two workgroups per CU)
+    constexpr int NG = Groups<T>::value;   // wavefront groups
+    constexpr int NBUF = 2;                // LDS buffers per operand and group
     constexpr int KD = NBUF == 4 ? 3 : 2;  // step t loads K tile t+KD
     constexpr int VD = NBUF == 4 ? 3 : 1;  // and V tile t+VD
     constexpr int N1 = NC * NBLK;          // Sᵀ MFMAs per tile
@@ -264,10 +272,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     constexpr int PF = 6;                  // operand prefetch distance (MFMAs)
     static_assert(NBUF * TILE_E * ES <= 65536, "buffer offsets fit the LDS immediate");
 
-    // K tiles [NBUF][BN][D], then V tiles [NBUF][BN][D], slots swizzled.
-    __shared__ __attribute__((aligned(1024))) T lds[2 * NBUF * TILE_E];
-    T* const lds_k = lds;
-    T* const lds_v = lds + NBUF * TILE_E;
+    // Per group: K tiles [NBUF][BN][D], then V tiles [NBUF][BN][D], slots
+    // swizzled.
+    __shared__ __attribute__((aligned(1024))) T lds[NG * 2 * NBUF * TILE_E];
 
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
@@ -283,13 +290,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
         task = wg / p.n_units;
         unit = wg % p.n_units;
     }
-    int qb = task;
-    if (CAUSAL) {
-        // two workgroups per CU: heaviest first for the first half of the
-        // launch, lightest first for the second half, so the pairs that share
-        // a CU even out
+    // With two groups a task is a pair of query blocks of one (batch, query
+    // head): under causal masking the heaviest and the lightest remaining
+    // block (qh = n_qb-1-task, ql = task), otherwise two neighbours.  Group 1
+    // takes the light block and then the first nb key tiles of the heavy
+    // block, group 0 the rest of the heavy block; nb evens out the two
+    // groups' tile counts, and the heavy block's two partial softmax states
+    // are merged through LDS at the end.  With one group a task is one block,
+    // heaviest first for the first half of the launch and lightest first for
+    // the second half (two workgroups per CU even out).
+    int qh = task, ql = -1;
+    if (NG == 2) {
+        if (CAUSAL) {
+            qh = p.n_qb - 1 - task;
+            ql = task < qh ? task : -1;
+        } else {
+            qh = 2 * task;
+            ql = 2 * task + 1 < p.n_qb ? 2 * task + 1 : -1;
+        }
+    } else if (CAUSAL) {
         const int half = (p.n_qb + 1) >> 1;
-        qb = task < half ? p.n_qb - 1 - task : task - half;
+        qh = task < half ? p.n_qb - 1 - task : task - half;
     }
     const int jg = unit % p.group;
     const int bg = unit / p.group;
@@ -303,17 +324,53 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
         const int L = p.pad_lens[b];
         key_lim = L < 0 ? 0 : (L > S ? S : L);
     }
-    int n = 0;  // key tiles with at least one visible key for this block
-    {
+    // key tiles with at least one visible key for query block q
+    auto tiles_of = [&](int q) __attribute__((always_inline)) {
+        if (q < 0) return 0;
         int e = key_lim;
-        if (CAUSAL) e = e < qb * BM + BM ? e : qb * BM + BM;
-        n = (e + BN - 1) / BN;
-    }
+        if (CAUSAL) e = e < q * BM + BM ? e : q * BM + BM;
+        return (e + BN - 1) / BN;
+    };
+    const int Th = tiles_of(qh);
+    const int Tl = tiles_of(ql);
+    int nb = 0;
+    if (NG == 2) nb = ql >= 0 ? (Th > Tl ? (Th - Tl) / 2 : 0) : Th / 2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // wavefront index, made provably uniform so branches on it are scalar
-    const int w4 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w4 = wave & 3;
+    const int grp = NG == 2 ? (wave >> 2) : 0;
+    T* const lds_k = lds + grp * 2 * NBUF * TILE_E;
+    T* const lds_v = lds_k + NBUF * TILE_E;
+
+    // this group's segments: (query block, key tiles [t0, t1), written out
+    // at its end or kept for the merge)
+    int nseg = 0, seg_q0 = 0, seg_a0 = 0, seg_b0 = 0, seg_q1 = 0, seg_a1 = 0, seg_b1 = 0;
+    bool seg_out0 = true, seg_out1 = true;
+    auto add_seg = [&](int q, int a, int e, bool out) __attribute__((always_inline)) {
+        if (nseg == 0) {
+            seg_q0 = q, seg_a0 = a, seg_b0 = e, seg_out0 = out;
+        } else {
+            seg_q1 = q, seg_a1 = a, seg_b1 = e, seg_out1 = out;
+        }
+        ++nseg;
+    };
+    if (grp == 0) {
+        add_seg(qh, nb, Th, nb == 0);
+    } else {
+        if (ql >= 0) add_seg(ql, 0, Tl, true);
+        if (nb > 0) add_seg(qh, 0, nb, false);
+    }
+    // barriers a segment of n tiles passes (initial loads, Sᵀ of its first
+    // tile, one per further tile); the groups pad to the same total
+    auto seg_bars = [](int n) { return n > 0 ? n + 1 : 0; };
+    const int bars0 = seg_bars(Th - nb);
+    const int bars1 = (ql >= 0 ? seg_bars(Tl) : 0) + (nb > 0 ? seg_bars(nb) : 0) + (ql >= 0 && nb > 0 ? 1 : 0);
+    const int bars_all = NG == 2 ? (bars0 > bars1 ? bars0 : bars1) : bars0;
+    int n_bar = 0;
+    int seg_end = 0;  // key tiles at or past this index are not loaded
     const int r = lane & 31;
     const int gl = lane >> 5;
 
@@ -348,24 +405,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
     const uint32_t ld_base = uint32_t(lr) * row_bytes + uint32_t((ps ^ swz<NS>(lr)) * 16);
     const uint32_t lds_k_b = uint32_t(reinterpret_cast<uintptr_t>(lds_k));
     const uint32_t lds_v_b = uint32_t(reinterpret_cast<uintptr_t>(lds_v));
-    // load i (0..2·NLD-1): K tile tk for i < NLD, else V tile tv; buffer
-    // tile % NBUF
-    auto load_one = [&](int tk, int tv, int i) __attribute__((always_inline)) {
-        const bool isv = i >= NLD;
-        const int t = isv ? tv : tk;
-        const int li = isv ? i - NLD : i;
+    // Buffer resource of one key tile: the slice from key row t·BN on, empty
+    // for a tile at or past the segment end (every lane then out of range, so
+    // the load writes zeros and reads no memory).  All scalar.
+    const uint64_t kaddr = reinterpret_cast<uint64_t>(kbase);
+    const uint64_t vaddr = reinterpret_cast<uint64_t>(vbase);
+    auto tile_rsrc = [&](uint64_t base, int t) __attribute__((always_inline)) {
+        const uint32_t off = uint32_t(t * BN) * row_bytes;
+        const bool live = t < seg_end && off < kv_bytes;
+        const uint64_t a = base + off;
+        return i32x4{__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
+                     __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff)),
+                     __builtin_amdgcn_readfirstlane(int(live ? kv_bytes - off : 0u)), 0x00020000};
+    };
+    const uint32_t lds_k_s = __builtin_amdgcn_readfirstlane(lds_k_b);
+    const uint32_t lds_v_s = __builtin_amdgcn_readfirstlane(lds_v_b);
+    // load li (0..NLD-1) of a tile with resource rs into LDS buffer buf
+    auto load_part = [&](const i32x4& rs, uint32_t lds_s, int buf, int li) __attribute__((always_inline)) {
         const int rw = (w4 * NLD + li) * RPL;
         uint32_t lb = ld_base;
         asm volatile("" : "+v"(lb));  // formed here, not hoisted as one register per load
-        const uint32_t voff = (lb ^ uint32_t(swz<NS>(rw) * 16)) + uint32_t(t * BN + rw) * row_bytes;
-        const uint32_t lds_byte = (isv ? lds_v_b : lds_k_b) + uint32_t((t & (NBUF - 1)) * TILE_E * ES) +
-                                  uint32_t((w4 * NLD + li) * 1024);
-        const bool live = t < n;
-        const i32x4 rv = isv ? (live ? vrs : vrs0) : (live ? krs : krs0);
-        // the selection is uniform; keep it in scalar registers
-        const i32x4 rs = {__builtin_amdgcn_readfirstlane(rv[0]), __builtin_amdgcn_readfirstlane(rv[1]),
-                          __builtin_amdgcn_readfirstlane(rv[2]), __builtin_amdgcn_readfirstlane(rv[3])};
-        lds_dma16(rs, __builtin_amdgcn_readfirstlane(lds_byte), voff);
+        const uint32_t voff = (lb ^ uint32_t(swz<NS>(rw) * 16)) + uint32_t(rw) * row_bytes;
+        lds_dma16(rs, lds_s + uint32_t(buf * TILE_E * ES) + uint32_t((w4 * NLD + li) * 1024), voff);
+    };
+    // load i (0..2·NLD-1): K tile tk for i < NLD, else V tile tv; buffer
+    // tile % NBUF
+    auto load_one = [&](int tk, int tv, int i) __attribute__((always_inline)) {
+        if (i < NLD)
+            load_part(tile_rsrc(kaddr, tk), lds_k_s, tk & (NBUF - 1), i);
+        else
+            load_part(tile_rsrc(vaddr, tv), lds_v_s, tv & (NBUF - 1), i - NLD);
     };
 
     // ---- per-lane LDS read offsets (elements, within a tile) ---------------
@@ -389,24 +458,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
         }
     const float sl2 = p.sl2;
 
-    // ---- this wave's 32 rows of the block -----------------------------------
-    const int wrow0 = qb * BM + w4 * 32;
-    const int qrow = wrow0 + r;
+    // ---- this wave's 32 rows of the current segment's block ----------------
+    int wrow0 = 0, qrow = 0;
     op_t qv[NC];
-    if (qrow < S) {
-        const T* qr = qbase + int64_t(qrow) * qstride;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) qv[c] = load_op<op_t>(qr + c * 2 * KPL + gl * KPL);
-    } else {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) qv[c] = op_t{};
-    }
     f32x16 oacc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY;  // running max (scaled, log2)
     float l_run = 0.0f;       // sum of the rounded probabilities
     float l_lse = 0.0f;       // sum of the exact probabilities (LSE)
+    auto begin_rows = [&](int q) __attribute__((always_inline)) {
+        wrow0 = q * BM + w4 * 32;
+        qrow = wrow0 + r;
+        if (qrow < S) {
+            const T* qr = qbase + int64_t(qrow) * qstride;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) qv[c] = load_op<op_t>(qr + c * 2 * KPL + gl * KPL);
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) qv[c] = op_t{};
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+        m_run = -INFINITY;
+        l_run = 0.0f;
+        l_lse = 0.0f;
+    };
 
     // normalise and store O (and LSE) for this wave's rows
     auto write_rows = [&]() __attribute__((always_inline)) {
@@ -649,64 +724,125 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(KParams p) {
         else
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's loads landed
         __syncthreads();
+        ++n_bar;
     };
 
-    // ---- prologue: K tiles 0..KD-1 and V tiles 0..VD-1 resident, Sᵀ(0) ------
+    // ---- the segments ---------------------------------------------------------
     f32x16 sa[NBLK], sb[NBLK];
-#pragma unroll
-    for (int t = 0; t < KD; ++t)
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) load_one(t, 0, i);
-#pragma unroll
-    for (int t = 0; t < VD; ++t)
-#pragma unroll
-        for (int i = NLD; i < 2 * NLD; ++i) load_one(0, t, i);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
-    __syncthreads();
-    if (n > 0) {
-        op_t fr[PF + 1];
-#pragma unroll
-        for (int f = 0; f < PF; ++f) fr[f] = fetch_k(lds_k, f);
-#pragma unroll
-        for (int i = 0; i < N1; ++i) {
-            if (i + PF < N1) fr[(i + PF) % (PF + 1)] = fetch_k(lds_k, i + PF);
-            if (i < NBLK)
-                mfma_zero(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
-            else
-                mfma_acc(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
-            __builtin_amdgcn_sched_barrier(0);
+    for (int sg = 0; sg < nseg; ++sg) {
+        const int q = sg == 0 ? seg_q0 : seg_q1;
+        const int t0 = sg == 0 ? seg_a0 : seg_a1;
+        const int t1 = sg == 0 ? seg_b0 : seg_b1;
+        const bool out = sg == 0 ? seg_out0 : seg_out1;
+        seg_end = t1;
+        if (sg > 0) {  // the previous segment's last step may still read the buffers
+            __syncthreads();
+            ++n_bar;
         }
-        // the first softmax reads these accumulators right away: wait out the
-        // MFMA result latency (the products are assembly, so the compiler
-        // does not insert these wait states itself)
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-        // step 0 reloads the buffer K tile 0 was read from
-        if constexpr (NBUF == 2) __syncthreads();
-        mask_tile(sa, 0);
+        begin_rows(q);
+        if (t0 < t1) {
+            // prologue: K tiles t0..t0+KD-1, V tiles t0..t0+VD-1 resident, Sᵀ(t0)
 #pragma unroll
-        for (int k = 0; k < NMX; ++k) max_item(sa, k);
-        fin0();
+            for (int k = 0; k < KD; ++k)
+#pragma unroll
+                for (int i = 0; i < NLD; ++i) load_one(t0 + k, 0, i);
+#pragma unroll
+            for (int k = 0; k < VD; ++k)
+#pragma unroll
+                for (int i = NLD; i < 2 * NLD; ++i) load_one(0, t0 + k, i);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
+            __syncthreads();
+            ++n_bar;
+            {
+                const T* k0 = lds_k + (t0 & (NBUF - 1)) * TILE_E;
+                op_t fr[PF + 1];
+#pragma unroll
+                for (int f = 0; f < PF; ++f) fr[f] = fetch_k(k0, f);
+#pragma unroll
+                for (int i = 0; i < N1; ++i) {
+                    if (i + PF < N1) fr[(i + PF) % (PF + 1)] = fetch_k(k0, i + PF);
+                    if (i < NBLK)
+                        mfma_zero(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                    else
+                        mfma_acc(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // the first softmax reads these accumulators right away: wait out
+            // the MFMA result latency (the products are assembly, so the
+            // compiler does not insert these wait states itself)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+            // step t0 reloads the buffer K tile t0 was read from
+            __syncthreads();
+            ++n_bar;
+            mask_tile(sa, t0);
+#pragma unroll
+            for (int k = 0; k < NMX; ++k) max_item(sa, k);
+            fin0();
 
-        // ---- steps 0 .. n-2 -------------------------------------------------
-        int t = 0;
-        for (; t + 1 < n; ++t) {
-            step(t, lds_k + ((t + 1) & (NBUF - 1)) * TILE_E, lds_v + (t & (NBUF - 1)) * TILE_E, sa, sb, true);
-            end_step();
-            // S(t+1) to the registers step t+1 reads; after the barrier, long
-            // after the MFMAs that wrote it
+            // steps t0 .. t1-2
+            int t = t0;
+            for (; t + 1 < t1; ++t) {
+                step(t, lds_k + ((t + 1) & (NBUF - 1)) * TILE_E, lds_v + (t & (NBUF - 1)) * TILE_E, sa, sb, true);
+                end_step();
+                // S(t+1) to the registers step t+1 reads; after the barrier,
+                // long after the MFMAs that wrote it
 #pragma unroll
-            for (int blk = 0; blk < NBLK; ++blk) {
-                asm volatile("" : "+v"(sb[blk]));
-                sa[blk] = sb[blk];
+                for (int blk = 0; blk < NBLK; ++blk) {
+                    asm volatile("" : "+v"(sb[blk]));
+                    sa[blk] = sb[blk];
+                }
+            }
+            // last step (t = t1-1): no next tile
+            step(t, lds_k, lds_v + (t & (NBUF - 1)) * TILE_E, sa, sb, false);
+            // the output accumulators were last written by MFMAs issued just
+            // now (wait states as after the prologue)
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+        }
+        if (out) write_rows();
+    }
+    // every wavefront passes the same number of barriers
+    for (; n_bar < bars_all; ++n_bar) __syncthreads();
+
+    // ---- merge the heavy block's two partial states ------------------------
+    // Group 1 leaves (m, l, O) of the heavy block's first nb tiles in LDS (its
+    // own tile buffers, idle now); group 0 combines them with its own:
+    // m = max(m0, m1), O = O0·2^(m0-m) + O1·2^(m1-m), likewise the sums.
+    if constexpr (NG == 2) {
+        if (nb > 0) {
+            constexpr int GRP_E = 2 * NBUF * TILE_E;  // elements per group region
+            float* stash_o = reinterpret_cast<float*>(lds + GRP_E);
+            float* stash_s = reinterpret_cast<float*>(lds);  // m, l, l_lse (group 0's region)
+            static_assert(4 * 64 * 16 * NDB * 4 <= GRP_E * ES, "O stash fits a group region");
+            if (grp == 1) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) stash_o[((w4 * NDB + db) * 16 + i) * 64 + lane] = oacc[db][i];
+                stash_s[(w4 * 3 + 0) * 64 + lane] = m_run;
+                stash_s[(w4 * 3 + 1) * 64 + lane] = l_run;
+                stash_s[(w4 * 3 + 2) * 64 + lane] = l_lse;
+            }
+            __syncthreads();
+            if (grp == 0) {
+                const float m1 = stash_s[(w4 * 3 + 0) * 64 + lane];
+                const float l1 = stash_s[(w4 * 3 + 1) * 64 + lane];
+                const float e1 = stash_s[(w4 * 3 + 2) * 64 + lane];
+                const float m = fmaxf(m_run, m1);
+                const float a0 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+                const float a1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        oacc[db][i] = oacc[db][i] * a0 + stash_o[((w4 * NDB + db) * 16 + i) * 64 + lane] * a1;
+                l_run = l_run * a0 + l1 * a1;
+                l_lse = l_lse * a0 + e1 * a1;
+                m_run = m;
+                write_rows();
             }
         }
-        // ---- last step (t = n-1): no next tile ----------------------------
-        step(t, lds_k, lds_v + (t & (NBUF - 1)) * TILE_E, sa, sb, false);
-        // the output accumulators were last written by MFMAs issued just now
-        // (wait states as after the prologue)
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
     }
-    write_rows();
 }
 
 template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
@@ -728,8 +864,10 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     kp.q_bstride = a.S * a.Hq * a.D;
     kp.kv_bstride = a.S * a.Hkv * a.D;
     kp.sl2 = a.scale * 1.44269504088896340736f;
-    const int64_t n_wg = int64_t(kp.n_qb) * kp.n_units;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD, LSE>), dim3(unsigned(n_wg)), dim3(kThreads), 0,
+    constexpr int NG = Groups<T>::value;
+    const int n_tasks = NG == 2 ? (kp.n_qb + 1) / 2 : kp.n_qb;
+    const int64_t n_wg = int64_t(n_tasks) * kp.n_units;
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD, LSE>), dim3(unsigned(n_wg)), dim3(kThreads * NG), 0,
                        static_cast<hipStream_t>(a.stream), kp);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return ATTN_OK;
