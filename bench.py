@@ -218,7 +218,11 @@ def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0):
                      "traffic": measured_traffic(w.name),
                      "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 3),
                      "flops_per_launch": fl,
-                     "min_hbm_bytes_per_launch": min_hbm_bytes(w, r["pad"])},
+                     "min_hbm_bytes_per_launch": min_hbm_bytes(w, r["pad"]),
+                     # the same launch against the HBM roofline (algorithmic bytes
+                     # over the kernel time), for shapes near the ridge
+                     "hbm_frac": round(min_hbm_bytes(w, r["pad"]) / (r["kernel_ms_mean"] * 1e-3) / 1e9
+                                       / HBM_PEAK_GBS, 4)},
     }
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(w)
@@ -238,6 +242,9 @@ def main():
                     help="time eager launches instead of a replayed HIP graph of the K steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="sequence-length sweep S = 1K..16K at B=1, H=32, D=128, bf16, causal "
+                         "(one line per S; an MFMA-bound kernel's time grows as S^2)")
     args = ap.parse_args()
     warmup_s = 0.5 if args.warmup is None else 0.0
     if args.warmup is None:
@@ -252,6 +259,19 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        from transformer_attention_06_amd import workloads as W
+        base = None
+        for S in (1024, 2048, 4096, 8192, 16384):
+            w = W.Workload(f"s_sweep_{S}", 4, B=1, S=S, Hq=32, Hkv=32, D=128, dtype="bf16", causal=True)
+            W.WORKLOADS[w.name] = w
+            line = bench_one(w.name, max(10, args.steps // (S // 1024)), args.warmup, False, not args.no_graph,
+                             warmup_s)
+            us = line["roofline"]["kernel_us_mean"]
+            base = base or (S, us)
+            line["config"]["time_vs_S2_scaling"] = round(us / (base[1] * (S / base[0]) ** 2), 3)
+            print(json.dumps(line), flush=True)
         return
     if args.all:
         from transformer_attention_06_amd import workloads as W
