@@ -543,14 +543,16 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
     auto mask_tile = [&](f32x16 (&s)[NBLK], int t) __attribute__((always_inline)) {
         const int kb = t * BN;
         if ((kb + BN > key_lim) || (CAUSAL && kb + BN - 1 > wrow0)) {
+            // key of register f = kb + 8·gl + kidx(f, 0); it is allowed below
+            // lim = min(key_lim, qrow + 1): one compare per score against a
+            // per-lane bound
+            const int lim = CAUSAL ? (key_lim < qrow + 1 ? key_lim : qrow + 1) : key_lim;
+            const int rel = lim - kb - 8 * gl;
 #pragma unroll
             for (int blk = 0; blk < NBLK; ++blk)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = kb + kidx(16 * blk + i, gl);
-                    const bool ok = key < key_lim && (!CAUSAL || key <= qrow);
-                    if (!ok) s[blk][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (kidx(16 * blk + i, 0) >= rel) s[blk][i] = -INFINITY;
         }
     };
     // Softmax work of one tile, split so it can ride along MFMAs:
