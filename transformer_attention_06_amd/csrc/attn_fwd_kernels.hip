@@ -428,13 +428,14 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
         const uint32_t voff = (lb ^ uint32_t(swz<NS>(rw) * 16)) + uint32_t(rw) * row_bytes;
         lds_dma16(rs, lds_s + uint32_t(buf * TILE_E * ES) + uint32_t((w4 * NLD + li) * 1024), voff);
     };
-    // load i (0..2·NLD-1): K tile tk for i < NLD, else V tile tv; buffer
-    // tile % NBUF
-    auto load_one = [&](int tk, int tv, int i) __attribute__((always_inline)) {
+    // load i (0..2·NLD-1): K tile tk into K buffer kbuf for i < NLD, else V
+    // tile tv into V buffer vbuf.  Buffers are counted from the segment's
+    // first tile, so that inside the two-step loop body they are constants.
+    auto load_one = [&](int tk, int tv, int kbuf, int vbuf, int i) __attribute__((always_inline)) {
         if (i < NLD)
-            load_part(tile_rsrc(kaddr, tk), lds_k_s, tk & (NBUF - 1), i);
+            load_part(tile_rsrc(kaddr, tk), lds_k_s, kbuf, i);
         else
-            load_part(tile_rsrc(vaddr, tv), lds_v_s, tv & (NBUF - 1), i - NLD);
+            load_part(tile_rsrc(vaddr, tv), lds_v_s, vbuf, i - NLD);
     };
 
     // ---- per-lane LDS read offsets (elements, within a tile) ---------------
@@ -643,12 +644,13 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
 
     // ---- one pipelined step --------------------------------------------------
     // Tile t: S(t) arrives in sc, already masked and with its row maxima
-    // taken (fin0 done); with G1, Sᵀ(t+1) is computed into sn from the K
-    // buffer (t+1) % NBUF.  One operand stream covers both parts: K operands
+    // taken (fin0 done); with G1, Sᵀ(t+1) is computed into sn from K buffer
+    // 1 - par.  One operand stream covers both parts: K operands
     // 0..N1-1, then V operands 0..N2-1, each read PF MFMAs ahead (the first V
     // operands while part A still runs).
     //   part A: Sᵀ(t+1) MFMAs; the running-max update, then the exponentials
-    //           of the first NKA P operands; loads of tile t+3;
+    //           of the first NKA P operands; loads of K tile t+2 and V
+    //           tile t+1;
     //   part B: P(t)·V(t) MFMAs; the exponentials of the other P operands,
     //           each finished NDB MFMAs before its first use; the mask and
     //           row maxima of S(t+1).
@@ -656,8 +658,13 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
     constexpr int NEA = NKA * KPL;         // their scores
     constexpr int MX0 = N2 / 8 > 1 ? N2 / 8 : 1;  // first part-B slot reading S(t+1)
     op_t pb[NKC];
-    auto step = [&](const int t, const T* kn, const T* vc, f32x16 (&sc)[NBLK], f32x16 (&sn)[NBLK],
+    // par: (t - first tile of the segment) % 2; K tile t+1 is in K buffer
+    // 1 - par, V tile t in V buffer par, and this step loads K tile t+2 into
+    // K buffer par and V tile t+1 into V buffer 1 - par.
+    auto step = [&](const int t, const int par, f32x16 (&sc)[NBLK], f32x16 (&sn)[NBLK],
                     const bool G1) __attribute__((always_inline)) {
+        const T* kn = lds_k + (1 - par) * TILE_E;
+        const T* vc = lds_v + par * TILE_E;
         constexpr int NL = 2 * NLD;
         static_assert(N1 % NL == 0, "loads spread evenly over part A");
         op_t fr[PF + 1];
@@ -672,7 +679,7 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
 #pragma unroll
         for (int i = 0; i < N1; ++i) {
             if (G1) {
-                if (i % (N1 / NL) == 0) load_one(t + KD, t + VD, i / (N1 / NL));
+                if (i % (N1 / NL) == 0) load_one(t + KD, t + VD, par, 1 - par, i / (N1 / NL));
                 if (i + PF < N1 + N2) fetch(i + PF);
                 if (i < NBLK)
                     mfma_zero(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
@@ -747,16 +754,16 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
 #pragma unroll
             for (int k = 0; k < KD; ++k)
 #pragma unroll
-                for (int i = 0; i < NLD; ++i) load_one(t0 + k, 0, i);
+                for (int i = 0; i < NLD; ++i) load_one(t0 + k, 0, k, 0, i);
 #pragma unroll
             for (int k = 0; k < VD; ++k)
 #pragma unroll
-                for (int i = NLD; i < 2 * NLD; ++i) load_one(0, t0 + k, i);
+                for (int i = NLD; i < 2 * NLD; ++i) load_one(0, t0 + k, 0, k, i);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
             __syncthreads();
             ++n_bar;
             {
-                const T* k0 = lds_k + (t0 & (NBUF - 1)) * TILE_E;
+                const T* k0 = lds_k;
                 op_t fr[PF + 1];
 #pragma unroll
                 for (int f = 0; f < PF; ++f) fr[f] = fetch_k(k0, f);
@@ -782,13 +789,21 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
             for (int k = 0; k < NMX; ++k) max_item(sa, k);
             fin0();
 
-            // steps t0 .. t1-2
+            // steps t0 .. t1-2, two per iteration: S alternates between sa
+            // and sb, and every buffer index is a constant
             int t = t0;
-            for (; t + 1 < t1; ++t) {
-                step(t, lds_k + ((t + 1) & (NBUF - 1)) * TILE_E, lds_v + (t & (NBUF - 1)) * TILE_E, sa, sb, true);
+            for (; t + 2 < t1; t += 2) {
+                step(t, 0, sa, sb, true);
                 end_step();
-                // S(t+1) to the registers step t+1 reads; after the barrier,
-                // long after the MFMAs that wrote it
+                step(t + 1, 1, sb, sa, true);
+                end_step();
+            }
+            if (t + 1 < t1) {
+                step(t, 0, sa, sb, true);
+                end_step();
+                ++t;
+                // S(t) to the registers the last step reads; after the
+                // barrier, long after the MFMAs that wrote it
 #pragma unroll
                 for (int blk = 0; blk < NBLK; ++blk) {
                     asm volatile("" : "+v"(sb[blk]));
@@ -796,7 +811,7 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
                 }
             }
             // last step (t = t1-1): no next tile
-            step(t, lds_k, lds_v + (t & (NBUF - 1)) * TILE_E, sa, sb, false);
+            step(t, (t - t0) & 1, sa, sb, false);
             // the output accumulators were last written by MFMAs issued just
             // now (wait states as after the prologue)
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
