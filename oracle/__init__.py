@@ -20,6 +20,9 @@ Pages cited (short name -> page title / address):
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (closed forms, invariants, an independent
 library routine and a high-precision brute force); none is "parity unpinned".
+The rotary embedding (``rope``) is pinned the same way by
+``tests/oracle_rope_pins.py`` (closed forms at D = 2, 4, 8, rotation
+invariants, the relative-position property and the complex-number form).
 """
 
 from .attention import (  # noqa: F401
@@ -31,4 +34,10 @@ from .attention import (  # noqa: F401
     attention_head,
     attention,
     attention_rows,
+)
+from .rope import (  # noqa: F401
+    DEFAULT_BASE as ROPE_DEFAULT_BASE,
+    rope_frequencies,
+    rope_positions,
+    rope,
 )

@@ -65,3 +65,48 @@ def test_mutant_is_caught(name):
             except (AssertionError, FloatingPointError, ValueError, IndexError) as e:
                 caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+# --------------------------------------------------------------------------
+# rotary embedding (oracle/rope.py) against tests/oracle_rope_pins.py
+# --------------------------------------------------------------------------
+import oracle_rope_pins  # noqa: E402
+
+ROPE_SRC = os.path.join(os.path.dirname(oracle.__file__), "rope.py")
+
+ROPE_MUTANTS = {
+    "sign_even": ("out[..., 0::2] = even * c - odd * sn", "out[..., 0::2] = even * c + odd * sn"),
+    "sign_odd": ("out[..., 1::2] = odd * c + even * sn", "out[..., 1::2] = odd * c - even * sn"),
+    "cos_sin_swapped": ("c = np.cos(ang)[:, :, None, :]", "c = np.sin(ang)[:, :, None, :]"),
+    "exponent_doubled": ("return np.power(float(base), -2.0 * i / d)", "return np.power(float(base), -4.0 * i / d)"),
+    "exponent_not_halved": ("return np.power(float(base), -2.0 * i / d)", "return np.power(float(base), -1.0 * i / d)"),
+    "base_ignored": ("return np.power(float(base), -2.0 * i / d)", "return np.power(10000.0, -2.0 * i / d)"),
+    "half_split_pairs": ("    even = x[..., 0::2]\n    odd = x[..., 1::2]",
+                         "    even = x[..., : d // 2]\n    odd = x[..., d // 2:]"),
+    "positions_ignored": ("    if positions is None:\n        return",
+                          "    if True:\n        return"),
+    "positions_batch0": ("    return pos\n", "    return np.broadcast_to(pos[0], (b, s))\n"),
+    "positions_from_one": ("return np.broadcast_to(np.arange(s, dtype=np.int64), (b, s))",
+                           "return np.broadcast_to(np.arange(1, s + 1, dtype=np.int64), (b, s))"),
+    "odd_not_rotated": ("out[..., 1::2] = odd * c + even * sn", "out[..., 1::2] = odd"),
+}
+
+
+def _load_rope_mutant(find, repl):
+    src = open(ROPE_SRC).read()
+    assert src.count(find) == 1, f"mutation anchor not unique/found: {find!r}"
+    mod = types.ModuleType("oracle_rope_mutant")
+    exec(compile(src.replace(find, repl), "oracle_rope_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_MUTANTS))
+def test_rope_mutant_is_caught(name):
+    mod = _load_rope_mutant(*ROPE_MUTANTS[name])
+    caught = []
+    for pin in oracle_rope_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except (AssertionError, FloatingPointError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"

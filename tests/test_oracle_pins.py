@@ -4,8 +4,14 @@ import pytest
 
 import oracle
 import oracle_pins
+import oracle_rope_pins
 
 
 @pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_pin(pin):
+    pin(oracle)
+
+
+@pytest.mark.parametrize("pin", oracle_rope_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_rope_pin(pin):
     pin(oracle)
