@@ -84,7 +84,8 @@ enum {
     ATTN_ERR_MASK = -6,        /* bad mask_kind / pad_lens / causal value      */
     ATTN_ERR_ALIGN = -7,       /* a data pointer is not 16-byte aligned        */
     ATTN_ERR_LAUNCH = -8,      /* the HIP launch failed                        */
-    ATTN_ERR_DEVICE = -9       /* the current device is not gfx950             */
+    ATTN_ERR_DEVICE = -9,      /* the current device is not gfx950             */
+    ATTN_ERR_ALIAS = -10       /* attn_fwd_rope: k_rot overlaps another tensor */
 };
 
 /*
@@ -116,6 +117,45 @@ int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t
              int mask_kind, const int32_t* pad_lens, float scale, int causal,
              int n_q_heads, int n_kv_heads,
              const attn_tensor_t* out, float* lse, void* stream);
+
+/*
+ * attn_fwd_rope — rotary position embedding of Q and K fused with attn_fwd.
+ *
+ * The fifth fusion pattern of the ATB engineering guide
+ * (hwcomputing.csdn.net/6a59a88310ee7a33f28e5ce9) §4.1 feeds RoPE(Q) and
+ * RoPE(K) into the attention without materialising rotated tensors; its §8.4
+ * configures the rotation (base 10000, interleaved pairs) and checks it
+ * against a plain rotation of each (even, odd) dimension pair.  Computed:
+ *
+ *   theta_i = base^(-2i/D),  i = 0 .. D/2-1
+ *   for Q and K, every head, row s of batch b at position p = positions[b,s]
+ *   (or p = s when positions is NULL):
+ *     x'[2i]   = x[2i]   cos(p theta_i) - x[2i+1] sin(p theta_i)
+ *     x'[2i+1] = x[2i+1] cos(p theta_i) + x[2i]   sin(p theta_i)
+ *   then attn_fwd(RoPE(Q), RoPE(K), V, ...) with every other argument as
+ *   attn_fwd documents.  The rotated values are rounded to the input dtype
+ *   before the products (as if RoPE ran as its own op); the angle is reduced
+ *   in fp64, so any int32 position is accurate.
+ *
+ * Two launches on `stream`: a bandwidth-bound pass writes RoPE(K) into k_rot
+ * (the form a KV cache keeps), then the attention kernel reads k_rot and
+ * rotates each Q tile in registers as it loads it (Q is never written).
+ *
+ *   positions   device int32[B, S] (4-byte aligned) or NULL for 0 .. S-1;
+ *               any int32 value is allowed.
+ *   rope_base   rotary base; any value that is not > 0 and finite selects
+ *               10000.
+ *   k_rot       output descriptor with the shape and dtype of k, 16-byte
+ *               aligned; receives RoPE(K).  It may be k itself (in-place
+ *               rotation); any other overlap with k, q, v, out or lse returns
+ *               ATTN_ERR_ALIAS.  Caller-owned like every other buffer.
+ *
+ * Returns ATTN_OK or a negative code; all checks run before any launch.
+ */
+int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                  int mask_kind, const int32_t* pad_lens, float scale, int causal,
+                  int n_q_heads, int n_kv_heads, const int32_t* positions, float rope_base,
+                  const attn_tensor_t* k_rot, const attn_tensor_t* out, float* lse, void* stream);
 
 /* Static, human-readable text for a return code (never NULL). */
 const char* attn_strerror(int code);

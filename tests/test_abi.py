@@ -150,3 +150,51 @@ def test_missing_library_fails_loudly(tmp_path):
             A.load_library(str(tmp_path / "nope.so"))
     finally:
         A._LIB = saved
+
+
+# --------------------------------------------------------------------------
+# attn_fwd_rope: the same checks plus its own (k_rot, positions), host only
+# --------------------------------------------------------------------------
+def call_rope(lib, q, k, v, out, k_rot, positions=None, base=0.0, lse=None, causal=0):
+    return lib.attn_fwd_rope(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0, None, ctypes.c_float(0.0),
+                             causal, q.H, k.H, positions, ctypes.c_float(base),
+                             ctypes.byref(k_rot) if k_rot is not None else None, ctypes.byref(out), lse, None)
+
+
+# four disjoint fake buffers (bf16, 1x8x2x64 = 2 KiB each)
+QA, KA, VA, OA, RA = (FAKE + i * 0x10000 for i in range(5))
+
+
+def test_rope_shares_attention_checks(lib):
+    assert call_rope(lib, T(H=4, data=QA), T(H=3, data=KA), T(H=3, data=VA), T(H=4, data=OA),
+                     T(H=3, data=RA)) == A.ATTN_ERR_HEADS
+    assert call_rope(lib, T(D=96, data=QA), T(D=96, data=KA), T(D=96, data=VA), T(D=96, data=OA),
+                     T(D=96, data=RA)) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_rope_k_rot_checks(lib):
+    args = (T(data=QA), T(data=KA), T(data=VA), T(data=OA))
+    assert call_rope(lib, *args, None) == A.ATTN_ERR_NULL
+    assert call_rope(lib, *args, T(data=0)) == A.ATTN_ERR_NULL
+    assert call_rope(lib, *args, T(data=RA, dtype=A.ATTN_F16)) == A.ATTN_ERR_DTYPE
+    assert call_rope(lib, *args, T(data=RA, S=9)) == A.ATTN_ERR_SHAPE
+    assert call_rope(lib, *args, T(data=RA, H=3)) == A.ATTN_ERR_SHAPE
+    assert call_rope(lib, *args, T(data=RA + 8)) == A.ATTN_ERR_ALIGN
+    assert call_rope(lib, *args, T(data=RA), positions=FAKE + 2) == A.ATTN_ERR_ALIGN
+
+
+def test_rope_aliasing(lib):
+    args = (T(data=QA), T(data=KA), T(data=VA), T(data=OA))
+    nbytes = 1 * 8 * 2 * 64 * 2
+    assert call_rope(lib, *args, T(data=QA)) == A.ATTN_ERR_ALIAS            # k_rot is q
+    assert call_rope(lib, *args, T(data=VA + 16)) == A.ATTN_ERR_ALIAS       # overlaps v
+    assert call_rope(lib, *args, T(data=OA - nbytes + 16)) == A.ATTN_ERR_ALIAS  # tail overlaps out
+    assert call_rope(lib, *args, T(data=KA + 16)) == A.ATTN_ERR_ALIAS       # part of k
+    assert call_rope(lib, *args, T(data=RA), lse=RA + 64) == A.ATTN_ERR_ALIAS
+
+
+def test_rope_empty_inputs_return_ok_without_launch(lib):
+    z = dict(S=0)
+    assert call_rope(lib, T(**z), T(**z), T(**z), T(**z), T(**z)) == A.ATTN_OK
+    z = dict(B=0, data=0)
+    assert call_rope(lib, T(**z), T(**z), T(**z), T(**z), T(**z)) == A.ATTN_OK

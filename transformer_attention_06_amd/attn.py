@@ -25,8 +25,9 @@ ATTN_ERR_MASK = -6
 ATTN_ERR_ALIGN = -7
 ATTN_ERR_LAUNCH = -8
 ATTN_ERR_DEVICE = -9
+ATTN_ERR_ALIAS = -10
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_strerror", "attn_version")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_rope", "attn_strerror", "attn_version")
 
 
 class AttnTensor(ctypes.Structure):
@@ -59,6 +60,10 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
                              ctypes.c_int, ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_rope.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, P, P,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd_rope.restype = ctypes.c_int
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -111,17 +116,8 @@ def describe(t):
     return AttnTensor(ctypes.c_void_p(t.data_ptr()), _dtype_code(t), b, s, h, d)
 
 
-def attn_fwd(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
-             stream=None):
-    """The C entry point with torch tensors: fills ``out`` (and ``lse``).
-
-    q, k, v, out: contiguous device tensors (B, S, H, D) of one dtype;
-    pad_lens: int32 device tensor [B] or None; lse: float32 device tensor
-    [B, n_q_heads, S] or None; scale: float (<= 0 or None selects 1/sqrt(D));
-    stream: a torch stream (default: the current stream).
-    """
+def _common_ptrs(q, k, v, out, pad_lens, lse, n_q_heads):
     import torch
-    lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
@@ -137,6 +133,53 @@ def attn_fwd(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads,
         if tuple(lse.shape) != (q.shape[0], n_q_heads, q.shape[1]):
             raise ValueError("lse must be [B, n_q_heads, S]")
         lse_ptr = ctypes.c_void_p(lse.data_ptr())
+    return pad_ptr, lse_ptr
+
+
+def attn_fwd_rope(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads, positions,
+                  rope_base, k_rot, out, lse, stream=None):
+    """``attn_fwd_rope`` with torch tensors: RoPE(K) into ``k_rot``, then the
+    attention of RoPE(Q), RoPE(K), V into ``out`` (and ``lse``).
+
+    positions: int32 device tensor [B, S] or None (0 .. S-1); rope_base:
+    float (None or <= 0 selects 10000); k_rot: tensor shaped like k (may be k).
+    """
+    import torch
+    lib = load_library()
+    pad_ptr, lse_ptr = _common_ptrs(q, k, v, out, pad_lens, lse, n_q_heads)
+    if not k_rot.is_cuda:
+        raise ValueError("k_rot must be a device tensor")
+    pos_ptr = None
+    if positions is not None:
+        if positions.dtype != torch.int32 or not positions.is_cuda or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int32 device tensor")
+        if tuple(positions.shape) != (q.shape[0], q.shape[1]):
+            raise ValueError("positions must be [B, S]")
+        pos_ptr = ctypes.c_void_p(positions.data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    dq, dk, dv, dkr, do = describe(q), describe(k), describe(v), describe(k_rot), describe(out)
+    code = lib.attn_fwd_rope(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(mask_kind), pad_ptr,
+                             ctypes.c_float(0.0 if scale is None else float(scale)), int(bool(causal)),
+                             int(n_q_heads), int(n_kv_heads), pos_ptr,
+                             ctypes.c_float(0.0 if rope_base is None else float(rope_base)),
+                             ctypes.byref(dkr), ctypes.byref(do), lse_ptr, ctypes.c_void_p(stream.cuda_stream))
+    check(code)
+    return out, k_rot, lse
+
+
+def attn_fwd(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
+             stream=None):
+    """The C entry point with torch tensors: fills ``out`` (and ``lse``).
+
+    q, k, v, out: contiguous device tensors (B, S, H, D) of one dtype;
+    pad_lens: int32 device tensor [B] or None; lse: float32 device tensor
+    [B, n_q_heads, S] or None; scale: float (<= 0 or None selects 1/sqrt(D));
+    stream: a torch stream (default: the current stream).
+    """
+    import torch
+    lib = load_library()
+    pad_ptr, lse_ptr = _common_ptrs(q, k, v, out, pad_lens, lse, n_q_heads)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
@@ -162,3 +205,19 @@ def flash_attention(q, k, v, *, causal=False, pad_lens=None, scale=None, return_
     mask_kind = ATTN_MASK_NONE if pad_lens is None else ATTN_MASK_KEY_PADDING
     attn_fwd(q, k, v, mask_kind, pad_lens, scale, causal, q.shape[2], k.shape[2], out, lse)
     return (out, lse) if return_lse else out
+
+
+def rope_attention(q, k, v, *, causal=False, pad_lens=None, scale=None, positions=None, rope_base=None,
+                   return_lse=False):
+    """Allocate ``out``, ``k_rot`` (and ``lse``) with torch and run
+    ``attn_fwd_rope``.  Returns (out, k_rot) or (out, k_rot, lse)."""
+    import torch
+    out = torch.empty_like(q)
+    k_rot = torch.empty_like(k)
+    lse = None
+    if return_lse:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    mask_kind = ATTN_MASK_NONE if pad_lens is None else ATTN_MASK_KEY_PADDING
+    attn_fwd_rope(q, k, v, mask_kind, pad_lens, scale, causal, q.shape[2], k.shape[2], positions, rope_base,
+                  k_rot, out, lse)
+    return (out, k_rot, lse) if return_lse else (out, k_rot)

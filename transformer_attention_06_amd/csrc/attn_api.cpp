@@ -18,12 +18,12 @@ bool valid_dtype(int32_t dt) { return dt == ATTN_F32 || dt == ATTN_F16 || dt == 
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-}  // namespace
-
-extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
-                        int mask_kind, const int32_t* pad_lens, float scale, int causal,
-                        int n_q_heads, int n_kv_heads, const attn_tensor_t* out, float* lse,
-                        void* stream) {
+// Checks every argument of attn_fwd and fills the launch struct; `empty` is
+// set when there is nothing to launch (B == 0 or S == 0).
+int prepare(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v, int mask_kind,
+            const int32_t* pad_lens, float scale, int causal, int n_q_heads, int n_kv_heads,
+            const attn_tensor_t* out, float* lse, void* stream, attn_detail::LaunchArgs& a, bool& empty) {
+    empty = false;
     if (!q || !k || !v || !out) return ATTN_ERR_NULL;
     if (!valid_dtype(q->dtype) || !valid_dtype(k->dtype) || !valid_dtype(v->dtype) ||
         !valid_dtype(out->dtype))
@@ -55,7 +55,10 @@ extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const at
     if (q->D != 64 && q->D != 128) return ATTN_ERR_UNSUPPORTED;
 
     const int64_t B = q->B, S = q->S, D = q->D;
-    if (B == 0 || S == 0) return ATTN_OK;  // empty input: nothing to launch
+    if (B == 0 || S == 0) {  // empty input: nothing to launch
+        empty = true;
+        return ATTN_OK;
+    }
 
     if (S >= (int64_t(1) << 29)) return ATTN_ERR_UNSUPPORTED;
     // Total element counts must stay far from int64 overflow.
@@ -76,7 +79,6 @@ extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const at
     float sc = scale;
     if (!(sc > 0.0f) || !std::isfinite(sc)) sc = 1.0f / std::sqrt(float(D));
 
-    attn_detail::LaunchArgs a;
     a.q = q->data;
     a.k = k->data;
     a.v = v->data;
@@ -93,6 +95,73 @@ extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const at
     a.padded = (mask_kind == ATTN_MASK_KEY_PADDING) ? 1 : 0;
     a.scale = sc;
     a.stream = stream;
+    return ATTN_OK;
+}
+
+bool overlap(const void* p, int64_t pn, const void* r, int64_t rn) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(r);
+    return a0 < b0 + uintptr_t(rn) && b0 < a0 + uintptr_t(pn);
+}
+
+int64_t bytes_of(const attn_tensor_t* t) {
+    return t->B * t->S * t->H * t->D * (t->dtype == ATTN_F32 ? 4 : 2);
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                        int mask_kind, const int32_t* pad_lens, float scale, int causal,
+                        int n_q_heads, int n_kv_heads, const attn_tensor_t* out, float* lse,
+                        void* stream) {
+    attn_detail::LaunchArgs a;
+    bool empty = false;
+    const int rc = prepare(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
+                           stream, a, empty);
+    if (rc != ATTN_OK || empty) return rc;
+    return attn_detail::launch(a);
+}
+
+// Rotary embedding of Q and K fused with the attention ([ATB-guide] §4.1,
+// fifth fusion pattern; §8.4 for the rotation and its base of 10000): K is
+// rotated once into k_rot by a bandwidth-bound pass, Q in registers inside
+// the attention kernel as its tile is loaded.
+extern "C" int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                             int mask_kind, const int32_t* pad_lens, float scale, int causal,
+                             int n_q_heads, int n_kv_heads, const int32_t* positions, float rope_base,
+                             const attn_tensor_t* k_rot, const attn_tensor_t* out, float* lse,
+                             void* stream) {
+    attn_detail::LaunchArgs a;
+    bool empty = false;
+    const int rc = prepare(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
+                           stream, a, empty);
+    if (rc != ATTN_OK) return rc;
+    if (!k_rot) return ATTN_ERR_NULL;
+    if (!valid_dtype(k_rot->dtype) || k_rot->dtype != k->dtype) return ATTN_ERR_DTYPE;
+    if (k_rot->B != k->B || k_rot->S != k->S || k_rot->H != k->H || k_rot->D != k->D) return ATTN_ERR_SHAPE;
+    if (empty) return ATTN_OK;
+    if (!k_rot->data) return ATTN_ERR_NULL;
+    if (!aligned16(k_rot->data)) return ATTN_ERR_ALIGN;
+    if (positions && (reinterpret_cast<uintptr_t>(positions) & 3u) != 0) return ATTN_ERR_ALIGN;
+    // k_rot is written before the attention reads q, v and writes out: it may
+    // be k itself, but must not overlap any other tensor (or k partially)
+    const int64_t kb = bytes_of(k_rot);
+    if (k_rot->data != k->data && overlap(k_rot->data, kb, k->data, bytes_of(k))) return ATTN_ERR_ALIAS;
+    if (overlap(k_rot->data, kb, q->data, bytes_of(q)) || overlap(k_rot->data, kb, v->data, bytes_of(v)) ||
+        overlap(k_rot->data, kb, out->data, bytes_of(out)))
+        return ATTN_ERR_ALIAS;
+    if (lse && overlap(k_rot->data, kb, lse, int64_t(sizeof(float)) * q->B * n_q_heads * q->S))
+        return ATTN_ERR_ALIAS;
+    double base = rope_base;
+    if (!(base > 0.0) || !std::isfinite(base)) base = 10000.0;
+    const int64_t D = q->D;
+    for (int64_t i = 0; i < D / 2; ++i)
+        a.rope_f[i] = std::pow(base, -2.0 * double(i) / double(D)) / (2.0 * 3.14159265358979323846);
+    a.rope_lb = std::log2(base);
+    a.rope_pos = positions;
+    a.rope = 1;
+    const int rk = attn_detail::launch_rope_k(a, k_rot->data);
+    if (rk != ATTN_OK) return rk;
+    a.k = k_rot->data;
     return attn_detail::launch(a);
 }
 
@@ -108,6 +177,7 @@ extern "C" const char* attn_strerror(int code) {
         case ATTN_ERR_ALIGN: return "a data pointer is not 16-byte aligned (pad_lens/lse: 4-byte)";
         case ATTN_ERR_LAUNCH: return "the HIP kernel launch failed";
         case ATTN_ERR_DEVICE: return "the current device cannot run this library's gfx950 code";
+        case ATTN_ERR_ALIAS: return "k_rot overlaps q, v, out, lse, or part of k (it may be k itself)";
         default: return "unknown error code";
     }
 }

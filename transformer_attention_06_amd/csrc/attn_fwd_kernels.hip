@@ -176,7 +176,27 @@ struct KParams {
     int S, Hq, Hkv, group, n_qb, n_units, xcd_chunk;
     int64_t q_bstride, kv_bstride;  // elements per batch
     float sl2;                      // scale * log2(e)
+    const int32_t* rope_pos;        // (B, S) positions, or null for 0..S-1
+    double rope_lb;                 // log2 of the rotary base
 };
+
+// Rotary embedding: cos and sin of position × theta_i, from f = theta_i / 2π.
+// The angle in turns is reduced to [-1/2, 1/2] in fp64, which is exact
+// enough for any int32 position; the 16-bit types then use the hardware sine
+// and cosine of a turn count (their error is far below the rounding of the
+// rotated value to 16 bits), fp32 the full-precision library sincos.
+template <typename T>
+__device__ __forceinline__ void rope_cs(int pos, double f, float& c, float& s) {
+    const double turns = double(pos) * f;
+    const double r = turns - __builtin_rint(turns);
+    if constexpr (sizeof(T) == 2) {
+        const float rf = float(r);
+        s = __builtin_amdgcn_sinf(rf);
+        c = __builtin_amdgcn_cosf(rf);
+    } else {
+        sincosf(float(r * 6.283185307179586476925), &s, &c);
+    }
+}
 
 template <typename T>
 __device__ __forceinline__ T to_t(float x) {
@@ -245,7 +265,7 @@ struct Groups {
 // tiles are double-buffered in LDS; step j loads K tile j+2 and V tile j+1
 // (one 1 KiB direct load per wavefront every few MFMAs) and ends with a wait
 // for those loads and one workgroup barrier.
-template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
+template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE>
 __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kernel(KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
@@ -476,6 +496,58 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
         } else {
 #pragma unroll
             for (int c = 0; c < NC; ++c) qv[c] = op_t{};
+        }
+        if constexpr (ROPE) {
+            // Rotary embedding of the Q tile in registers ([ATB-guide] §4.1
+            // fifth fusion pattern, §8.4): pair (2i, 2i+1) turns by the row's
+            // position × theta_i; the rotated values are rounded to T, as the
+            // MFMA operand.
+            const int pos = qrow < S ? (p.rope_pos ? p.rope_pos[int64_t(b) * S + qrow] : qrow) : 0;
+            // theta_i = rho^i with rho = base^(-2/D), formed here from an
+            // opaque copy of log2(base) so that nothing stays live across the
+            // tile loop
+            double lb = p.rope_lb;
+            asm volatile("" : "+v"(lb));
+            const double r1 = exp2(lb * (-2.0 / D));
+            const double r4 = (r1 * r1) * (r1 * r1);
+            const double r8 = r4 * r4;
+            if constexpr (KPL == 1) {
+                // lane gl holds dimension 2c + gl: the pair's other half sits
+                // in the lane 32 away
+                // theta_i / 2pi = rho^i / 2pi, stepped by multiplication
+                double f = 0.15915494309189533577;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    asm volatile("" : "+v"(f));  // one pair at a time: bounded registers
+                    float cs, sn;
+                    rope_cs<T>(pos, f, cs, sn);
+                    f *= r1;
+                    const float mine = qv[c];
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mine), __float_as_uint(mine),
+                                                                     false, false);
+                    const float other = __uint_as_float(gl == 0 ? sw[1] : sw[0]);
+                    qv[c] = gl == 0 ? mine * cs - other * sn : mine * cs + other * sn;
+                }
+            } else {
+                // lane holds dimensions 16c + 8gl + 0..7: pairs 8c + 4gl + 0..3;
+                // theta_i / 2pi = rho^i / 2pi, stepped by multiplication
+                double fc = gl ? 0.15915494309189533577 * r4 : 0.15915494309189533577;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    double f = fc;
+#pragma unroll
+                    for (int j = 0; j < KPL / 2; ++j) {
+                        asm volatile("" : "+v"(f));  // one pair at a time: bounded registers
+                        float cs, sn;
+                        rope_cs<T>(pos, f, cs, sn);
+                        const float x0 = float(qv[c][2 * j]), x1 = float(qv[c][2 * j + 1]);
+                        qv[c][2 * j] = to_t<T>(x0 * cs - x1 * sn);
+                        qv[c][2 * j + 1] = to_t<T>(x1 * cs + x0 * sn);
+                        f *= r1;
+                    }
+                    fc *= r8;
+                }
+            }
         }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
@@ -862,7 +934,7 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool PAD, bool LSE>
+template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE>
 int launch_t(const attn_detail::LaunchArgs& a) {
     KParams kp;
     kp.q = a.q;
@@ -881,10 +953,12 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     kp.q_bstride = a.S * a.Hq * a.D;
     kp.kv_bstride = a.S * a.Hkv * a.D;
     kp.sl2 = a.scale * 1.44269504088896340736f;
+    kp.rope_pos = a.rope_pos;
+    kp.rope_lb = a.rope_lb;
     constexpr int NG = Groups<T>::value;
     const int n_tasks = NG == 2 ? (kp.n_qb + 1) / 2 : kp.n_qb;
     const int64_t n_wg = int64_t(n_tasks) * kp.n_units;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD, LSE>), dim3(unsigned(n_wg)), dim3(kThreads * NG), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD, LSE, ROPE>), dim3(unsigned(n_wg)), dim3(kThreads * NG), 0,
                        static_cast<hipStream_t>(a.stream), kp);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return ATTN_OK;
@@ -892,10 +966,15 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     return ATTN_ERR_LAUNCH;
 }
 
+template <typename T, int D, bool LSE, bool ROPE>
+int launch_r(const attn_detail::LaunchArgs& a) {
+    if (a.causal) return a.padded ? launch_t<T, D, true, true, LSE, ROPE>(a) : launch_t<T, D, true, false, LSE, ROPE>(a);
+    return a.padded ? launch_t<T, D, false, true, LSE, ROPE>(a) : launch_t<T, D, false, false, LSE, ROPE>(a);
+}
+
 template <typename T, int D, bool LSE>
 int launch_l(const attn_detail::LaunchArgs& a) {
-    if (a.causal) return a.padded ? launch_t<T, D, true, true, LSE>(a) : launch_t<T, D, true, false, LSE>(a);
-    return a.padded ? launch_t<T, D, false, true, LSE>(a) : launch_t<T, D, false, false, LSE>(a);
+    return a.rope ? launch_r<T, D, LSE, true>(a) : launch_r<T, D, LSE, false>(a);
 }
 
 template <typename T, int D>
@@ -908,9 +987,107 @@ int launch_dtype(const attn_detail::LaunchArgs& a) {
     return a.D == 64 ? launch_d<T, 64>(a) : launch_d<T, 128>(a);
 }
 
+// Rotary embedding of K into K_rot, both (B, S, Hkv, D) ([ATB-guide] §8.4,
+// the K half of §4.1's fifth fusion pattern).  An HBM-bound pass: one thread
+// per (row, 16-byte chunk of a head row, group of up to 8 kv heads); the
+// chunk's cos/sin are computed once and applied to every head of the group,
+// whose 16-byte loads are all issued before the first store.  Each thread
+// reads and writes the same chunks, so K_rot may be K itself.
+struct RopeKParams {
+    const void* k;
+    void* k_out;
+    const int32_t* pos;
+    int64_t rows;  // B * S
+    int S, Hkv, n_hg;
+    double f[64];  // theta_i / 2pi, i < D/2
+};
+
+constexpr int kRopeHeads = 8;  // kv heads per thread
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_k_kernel(RopeKParams rp) {
+    constexpr int CH = 16 / int(sizeof(T));  // elements per chunk
+    constexpr int NCH = D / CH;              // chunks per head row
+    constexpr int NP = CH / 2;               // pairs per chunk
+    __shared__ double f_s[D / 2];
+    if (threadIdx.x < D / 2) f_s[threadIdx.x] = rp.f[threadIdx.x];
+    __syncthreads();
+    const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    const int chunk = int(gid % NCH);
+    const int64_t rest = gid / NCH;
+    const int hg = int(rest % rp.n_hg);
+    const int64_t row = rest / rp.n_hg;  // b * S + s
+    if (row >= rp.rows) return;
+    const int pos = rp.pos ? rp.pos[row] : int(row % rp.S);
+    float cs[NP], sn[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) rope_cs<T>(pos, f_s[chunk * NP + j], cs[j], sn[j]);
+    const int h0 = hg * kRopeHeads;
+    const int nh = rp.Hkv - h0 < kRopeHeads ? rp.Hkv - h0 : kRopeHeads;
+    const int64_t base = (row * rp.Hkv + h0) * D + int64_t(chunk) * CH;
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const T*>(rp.k) + base);
+    u32x4* dst = reinterpret_cast<u32x4*>(static_cast<T*>(rp.k_out) + base);
+    constexpr int STEP = D / CH;  // u32x4 per head row
+    u32x4 v[kRopeHeads];
+#pragma unroll
+    for (int h = 0; h < kRopeHeads; ++h)
+        if (h < nh) v[h] = src[h * STEP];
+#pragma unroll
+    for (int h = 0; h < kRopeHeads; ++h) {
+        if (h < nh) {
+            T x[CH];
+            __builtin_memcpy(x, &v[h], 16);
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                const float x0 = float(x[2 * j]), x1 = float(x[2 * j + 1]);
+                x[2 * j] = to_t<T>(x0 * cs[j] - x1 * sn[j]);
+                x[2 * j + 1] = to_t<T>(x1 * cs[j] + x0 * sn[j]);
+            }
+            u32x4 o;
+            __builtin_memcpy(&o, x, 16);
+            dst[h * STEP] = o;
+        }
+    }
+}
+
+template <typename T, int D>
+int launch_rope_t(const attn_detail::LaunchArgs& a, void* k_out) {
+    RopeKParams rp;
+    rp.k = a.k;
+    rp.k_out = k_out;
+    rp.pos = a.rope_pos;
+    rp.rows = a.B * a.S;
+    rp.S = int(a.S);
+    rp.Hkv = int(a.Hkv);
+    rp.n_hg = int((a.Hkv + kRopeHeads - 1) / kRopeHeads);
+    for (int i = 0; i < 64; ++i) rp.f[i] = i < D / 2 ? a.rope_f[i] : 0.0;
+    constexpr int NCH = D / (16 / int(sizeof(T)));
+    const int64_t threads = rp.rows * rp.n_hg * NCH;
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL((rope_k_kernel<T, D>), dim3(unsigned(blocks)), dim3(256), 0,
+                       static_cast<hipStream_t>(a.stream), rp);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return ATTN_OK;
+    if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction) return ATTN_ERR_DEVICE;
+    return ATTN_ERR_LAUNCH;
+}
+
+template <typename T>
+int launch_rope_dtype(const attn_detail::LaunchArgs& a, void* k_out) {
+    return a.D == 64 ? launch_rope_t<T, 64>(a, k_out) : launch_rope_t<T, 128>(a, k_out);
+}
+
 }  // namespace
 
 namespace attn_detail {
+
+int launch_rope_k(const LaunchArgs& a, void* k_out) {
+    switch (a.dtype) {
+        case ATTN_BF16: return launch_rope_dtype<__bf16>(a, k_out);
+        case ATTN_F16: return launch_rope_dtype<_Float16>(a, k_out);
+        default: return launch_rope_dtype<float>(a, k_out);
+    }
+}
 
 int launch(const LaunchArgs& a) {
     switch (a.dtype) {

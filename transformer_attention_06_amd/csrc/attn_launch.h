@@ -22,9 +22,19 @@ struct LaunchArgs {
     int padded;
     float scale;
     void* stream;
+    // rotary embedding of Q inside the attention kernel (K is rotated
+    // beforehand by launch_rope_k)
+    int rope = 0;
+    const int32_t* rope_pos = nullptr;  // (B, S) positions or null (0..S-1)
+    double rope_f[64] = {};             // theta_i / 2pi for i < D/2
+    double rope_lb = 0.0;               // log2(base): theta_i = 2^(-2i/D * rope_lb)
 };
 
 // Enqueue the kernel; returns ATTN_OK or ATTN_ERR_LAUNCH / ATTN_ERR_DEVICE.
 int launch(const LaunchArgs& a);
+
+// Enqueue the rotary embedding of K (a.k, layout (B, S, Hkv, D)) into
+// k_out (same layout; may be a.k itself) with a.rope_pos and a.rope_f.
+int launch_rope_k(const LaunchArgs& a, void* k_out);
 
 }  // namespace attn_detail
