@@ -15,7 +15,7 @@ kernel source, else null.  The cpu_baseline block times the fp64 CPU oracle on
 a bounded sample of heads of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--all] [--copy-calibration]
+                    [--no-cpu-baseline] [--all] [--sweep] [--rope] [--copy-calibration]
 """
 
 import argparse
@@ -50,7 +50,7 @@ def min_hbm_bytes(w, pad):
     return qo + kv + lse
 
 
-def run_gpu(w, steps, warmup, use_graph=True, warmup_s=0.0):
+def run_gpu(w, steps, warmup, use_graph=True, warmup_s=0.0, rope=False):
     import torch
     from transformer_attention_06_amd import attn as A
     from transformer_attention_06_amd import workloads as W
@@ -65,9 +65,13 @@ def run_gpu(w, steps, warmup, use_graph=True, warmup_s=0.0):
     out = torch.empty_like(qd)
     lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device="cuda") if w.want_lse else None
     mask = A.ATTN_MASK_NONE if pad is None else A.ATTN_MASK_KEY_PADDING
+    k_rot = torch.empty_like(kd) if rope else None
     def step():
         # launches on the current stream (the capture stream while capturing)
-        A.attn_fwd(qd, kd, vd, mask, pad_d, None, w.causal, w.Hq, w.Hkv, out, lse)
+        if rope:  # rotary pass over K, then the attention with Q rotated at load
+            A.attn_fwd_rope(qd, kd, vd, mask, pad_d, None, w.causal, w.Hq, w.Hkv, None, None, k_rot, out, lse)
+        else:
+            A.attn_fwd(qd, kd, vd, mask, pad_d, None, w.causal, w.Hq, w.Hkv, out, lse)
 
     # Untimed warmup: at least `warmup` steps, and (by default) at least half
     # a second of them, so the timed region starts at a settled clock.
@@ -188,10 +192,10 @@ def cpu_baseline(w, budget_s=12.0):
                       f"full SxS score matrix, {el:.2f} s wall"}
 
 
-def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0):
+def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0, rope=False):
     from transformer_attention_06_amd import workloads as W
     w = W.WORKLOADS[name]
-    r = run_gpu(w, steps, warmup, use_graph, warmup_s)
+    r = run_gpu(w, steps, warmup, use_graph, warmup_s, rope=rope)
     fl = metric_flops(w)
     value = fl / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = fl / (r["kernel_ms_mean"] * 1e-3) / 1e12
@@ -211,7 +215,8 @@ def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0):
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape; no weights)",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "causal": w.causal, "mask": "key_padding" if w.mask_kind else "none",
-                   "lse": w.want_lse, "timing": "hip_graph_replay" if use_graph else "eager_launches",
+                   "lse": w.want_lse, "rope": rope,
+                   "timing": "hip_graph_replay" if use_graph else "eager_launches",
                    "pct_of_peak_wall": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
@@ -224,6 +229,20 @@ def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0):
                      "hbm_frac": round(min_hbm_bytes(w, r["pad"]) / (r["kernel_ms_mean"] * 1e-3) / 1e9
                                        / HBM_PEAK_GBS, 4)},
     }
+    if rope:
+        # the call is two launches: the K rotation pass (bandwidth-bound: K
+        # read and written once) and the attention with Q rotated at load;
+        # the plain attention on the same inputs gives the cost of both
+        r0 = run_gpu(w, steps, warmup, use_graph, warmup_s, rope=False)
+        el = {"bf16": 2, "fp16": 2, "fp32": 4}[w.dtype]
+        kbytes = 2 * w.B * w.S * w.Hkv * w.D * el
+        extra_us = (r["kernel_ms_mean"] - r0["kernel_ms_mean"]) * 1e3
+        line["roofline"]["traffic"] = None
+        line["rope"] = {"call_us_mean": round(r["kernel_ms_mean"] * 1e3, 3),
+                        "attn_fwd_us_mean": round(r0["kernel_ms_mean"] * 1e3, 3),
+                        "extra_us": round(extra_us, 3),
+                        "k_pass_bytes": kbytes,
+                        "k_pass_min_us_at_8TBps": round(kbytes / (HBM_PEAK_GBS * 1e3), 3)}
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(w)
     return line
@@ -242,6 +261,8 @@ def main():
                     help="time eager launches instead of a replayed HIP graph of the K steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--rope", action="store_true",
+                    help="time attn_fwd_rope (rotary embedding of Q and K fused with the attention)")
     ap.add_argument("--sweep", action="store_true",
                     help="sequence-length sweep S = 1K..16K at B=1, H=32, D=128, bf16, causal "
                          "(one line per S; an MFMA-bound kernel's time grows as S^2)")
@@ -277,9 +298,11 @@ def main():
         from transformer_attention_06_amd import workloads as W
         for name in W.WORKLOADS:
             print(json.dumps(bench_one(name, args.steps, args.warmup, False, not args.no_graph, warmup_s)), flush=True)
+        print(json.dumps(bench_one(DEFAULT_WORKLOAD, args.steps, args.warmup, False, not args.no_graph, warmup_s,
+                                   rope=True)), flush=True)
         return
-    print(json.dumps(bench_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline,
-                               not args.no_graph, warmup_s)), flush=True)
+    print(json.dumps(bench_one(args.workload, args.steps, args.warmup, not args.no_cpu_baseline and not args.rope,
+                               not args.no_graph, warmup_s, rope=args.rope)), flush=True)
 
 
 if __name__ == "__main__":
