@@ -22,7 +22,10 @@ Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 library routine and a high-precision brute force); none is "parity unpinned".
 The rotary embedding (``rope``) is pinned the same way by
 ``tests/oracle_rope_pins.py`` (closed forms at D = 2, 4, 8, rotation
-invariants, the relative-position property and the complex-number form).
+invariants, the relative-position property and the complex-number form), and
+decode attention over a KV cache (``attention_decode``) by
+``tests/oracle_decode_pins.py`` (equality with the last rows of a prefill,
+cache truncation, the key-split merge by LSE, torch's SDPA).
 """
 
 from .attention import (  # noqa: F401
@@ -40,4 +43,8 @@ from .rope import (  # noqa: F401
     rope_frequencies,
     rope_positions,
     rope,
+)
+from .decode import (  # noqa: F401
+    visible_keys as decode_visible_keys,
+    attention_decode,
 )

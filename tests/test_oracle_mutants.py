@@ -110,3 +110,48 @@ def test_rope_mutant_is_caught(name):
         except (AssertionError, FloatingPointError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+# --------------------------------------------------------------------------
+# decode attention (oracle/decode.py) against tests/oracle_decode_pins.py
+# --------------------------------------------------------------------------
+import oracle_decode_pins  # noqa: E402
+
+DECODE_SRC = os.path.join(os.path.dirname(oracle.__file__), "decode.py")
+
+DECODE_MUTANTS = {
+    "top_left_alignment": ("return j <= key_len - sq + i", "return j <= i"),
+    "alignment_off_by_one": ("return j <= key_len - sq + i", "return j < key_len - sq + i"),
+    "alignment_past_end": ("return j <= key_len - sq + i", "return j <= key_len - sq + i + 1"),
+    "cache_lens_ignored": ("L = sk if cache_lens is None else", "L = sk if True else"),
+    "cache_lens_batch0": ("int(min(max(int(cache_lens[b]), 0), sk))", "int(min(max(int(cache_lens[0]), 0), sk))"),
+    "non_causal_sees_nothing_past_query": ("        return np.ones(key_len, dtype=bool)",
+                                           "        return np.arange(key_len) <= i"),
+    "lse_missing_max": ("lse[b, h, i] = m + np.log(den)", "lse[b, h, i] = np.log(den)"),
+    "dropped_scale": ("s = (kh[ok] @ q[b, i, h, :]) * scale", "s = (kh[ok] @ q[b, i, h, :])"),
+    "unnormalised": ("out[b, i, h, :] = (e / den) @ vh[ok]", "out[b, i, h, :] = e @ vh[ok]"),
+    "gqa_wrong_head": ("g = kv_head_for(h, hq, hkv)", "g = h % hkv"),
+}
+
+
+def _load_decode_mutant(find, repl):
+    src = open(DECODE_SRC).read()
+    assert src.count(find) == 1, f"mutation anchor not unique/found: {find!r}"
+    src = src.replace(find, repl).replace("from .attention import", "from oracle.attention import")
+    mod = types.ModuleType("oracle_decode_mutant")
+    exec(compile(src, "oracle_decode_mutant.py", "exec"), mod.__dict__)
+    # the pins also use the (pinned) prefill oracle through the same module
+    mod.attention = oracle.attention
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_MUTANTS))
+def test_decode_mutant_is_caught(name):
+    mod = _load_decode_mutant(*DECODE_MUTANTS[name])
+    caught = []
+    for pin in oracle_decode_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except (AssertionError, FloatingPointError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"

@@ -3,6 +3,7 @@
 import pytest
 
 import oracle
+import oracle_decode_pins
 import oracle_pins
 import oracle_rope_pins
 
@@ -14,4 +15,9 @@ def test_pin(pin):
 
 @pytest.mark.parametrize("pin", oracle_rope_pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_rope_pin(pin):
+    pin(oracle)
+
+
+@pytest.mark.parametrize("pin", oracle_decode_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_decode_pin(pin):
     pin(oracle)
