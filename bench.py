@@ -15,7 +15,7 @@ kernel source, else null.  The cpu_baseline block times the fp64 CPU oracle on
 a bounded sample of heads of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--all] [--sweep] [--rope] [--copy-calibration]
+                    [--no-cpu-baseline] [--all] [--sweep] [--rope] [--decode] [--copy-calibration]
 """
 
 import argparse
@@ -192,6 +192,83 @@ def cpu_baseline(w, budget_s=12.0):
                       f"full SxS score matrix, {el:.2f} s wall"}
 
 
+DECODE_SHAPES = {
+    # Llama-2-70B-shaped decode step: one new token per sequence against a
+    # 4096-token KV cache (64 query heads sharing 8 kv heads, D = 128, bf16)
+    "llama2_70b_decode_b8": dict(B=8, Sq=1, Sk=4096, Hq=64, Hkv=8, D=128),
+    "llama2_70b_decode_b2": dict(B=2, Sq=1, Sk=4096, Hq=64, Hkv=8, D=128),
+}
+
+
+def bench_decode(name, steps, warmup, use_graph=True, warmup_s=0.0):
+    """Decode attention over a KV cache (split-KV + merge): bound by reading
+    the cache, so the figure is algorithmic bytes (K, V caches, Q, O, LSE)
+    per call against the HBM peak."""
+    import torch
+    from transformer_attention_06_amd import attn as A
+    sh = DECODE_SHAPES[name]
+    B, Sq, Sk, Hq, Hkv, D = (sh[x] for x in ("B", "Sq", "Sk", "Hq", "Hkv", "D"))
+    g = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.randn(B, Sq, Hq, D, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Sk, Hkv, D, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Sk, Hkv, D, device="cuda", generator=g).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, Sq, device="cuda", dtype=torch.float32)
+    ws = torch.empty(A.decode_workspace_bytes(B, Sq, Hq, D, Sk), dtype=torch.uint8, device="cuda")
+
+    def step():
+        A.attn_fwd_decode(q, k, v, None, None, True, Hq, Hkv, out, lse, ws)
+
+    t_w = time.perf_counter()
+    done = 0
+    while done < warmup or (warmup_s > 0 and time.perf_counter() - t_w < warmup_s):
+        step()
+        done += 1
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                step()
+        graph.replay()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(steps):
+            step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_wall = (t1 - t0) * 1e3 / steps
+    ms_dev = e0.elapsed_time(e1) / steps
+    nbytes = 2 * B * Sk * Hkv * D * 2 + 2 * B * Sq * Hq * D * 2 + B * Hq * Sq * 4
+    gbs = nbytes / (ms_wall * 1e-3) / 1e9
+    achieved = nbytes / (ms_dev * 1e-3) / 1e9
+    return {"metric": "decode attention over a KV cache: algorithmic HBM GB/s", "value": round(gbs, 2),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": done, "ms_per_step": round(ms_wall, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) query, K cache and V cache)",
+            "config": {"workload": name, **sh, "causal": True, "timing": "hip_graph_replay" if use_graph
+                       else "eager_launches", "launches_per_call": 2},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "call_us_mean": round(ms_dev * 1e3, 3), "algorithmic_bytes_per_call": nbytes,
+                         "workspace_bytes": int(ws.numel())}}
+
+
 def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0, rope=False):
     from transformer_attention_06_amd import workloads as W
     w = W.WORKLOADS[name]
@@ -261,6 +338,8 @@ def main():
                     help="time eager launches instead of a replayed HIP graph of the K steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--decode", action="store_true",
+                    help="decode attention over a KV cache (attn_fwd_decode), Llama-2-70B shapes, HBM roofline")
     ap.add_argument("--rope", action="store_true",
                     help="time attn_fwd_rope (rotary embedding of Q and K fused with the attention)")
     ap.add_argument("--sweep", action="store_true",
@@ -280,6 +359,10 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.decode:
+        for name in DECODE_SHAPES:
+            print(json.dumps(bench_decode(name, args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)
         return
     if args.sweep:
         from transformer_attention_06_amd import workloads as W

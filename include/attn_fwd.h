@@ -85,7 +85,8 @@ enum {
     ATTN_ERR_ALIGN = -7,       /* a data pointer is not 16-byte aligned        */
     ATTN_ERR_LAUNCH = -8,      /* the HIP launch failed                        */
     ATTN_ERR_DEVICE = -9,      /* the current device is not gfx950             */
-    ATTN_ERR_ALIAS = -10       /* attn_fwd_rope: k_rot overlaps another tensor */
+    ATTN_ERR_ALIAS = -10,      /* attn_fwd_rope: k_rot overlaps another tensor */
+    ATTN_ERR_WORKSPACE = -11   /* attn_fwd_decode: workspace too small         */
 };
 
 /*
@@ -156,6 +157,49 @@ int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, const attn_ten
                   int mask_kind, const int32_t* pad_lens, float scale, int causal,
                   int n_q_heads, int n_kv_heads, const int32_t* positions, float rope_base,
                   const attn_tensor_t* k_rot, const attn_tensor_t* out, float* lse, void* stream);
+
+/*
+ * attn_fwd_decode — decode attention over a KV cache (split over key chunks).
+ *
+ * The serving step the pages build around a KV cache: the ATB introduction
+ * (hwcomputing.csdn.net/6a15a709662f9a54cb774da1) runs a causal
+ * FlashAttention with KV-cache management on, and "CANN-ops-transformer和
+ * ATB-昇腾NPU上算子和加速库怎么配合" has ATB pass the cache into and out of
+ * FlashAttention on every generation step.  Computed, for every batch b,
+ * query head h (kv head g = floor(h*Hkv/Hq)) and new row i < Sq:
+ *
+ *   L_b = cache_lens[b] clamped to [0, Sk]   (Sk when cache_lens is NULL)
+ *   key j is visible iff j < L_b and, when causal, j <= L_b - Sq + i
+ *     (the new rows are the last Sq positions of the sequence)
+ *   O[b,i,h,:] = softmax_j(scale · q·k_j) · V,  LSE[b,h,i] = ln Σ_j exp(scale · q·k_j)
+ *   (a row with no visible key: O = 0, LSE = -inf)
+ *
+ *   q, out      (B, Sq, Hq, D) descriptors; k_cache, v_cache (B, Sk, Hkv, D),
+ *               Sk may differ from Sq; dtype and D as for attn_fwd.
+ *   cache_lens  device int32[B] (4-byte aligned) or NULL.
+ *   scale, causal, n_q_heads, n_kv_heads, lse, stream: as for attn_fwd
+ *               (lse is (B, Hq, Sq)).
+ *   workspace   caller-owned device buffer, 16-byte aligned, of at least
+ *               attn_decode_workspace_bytes(B, Sq, Hq, D, Sk) bytes (else
+ *               ATTN_ERR_WORKSPACE); it holds per-chunk partial results
+ *               between the two launches, so calls that share a workspace
+ *               must not overlap.
+ *
+ * Two launches on `stream`: one workgroup per (256-key chunk, batch, kv head,
+ * 8 query rows) writes the chunk's partial (O, max, sum); a merge kernel
+ * combines the chunks by their log-sum-exp and writes O and LSE.
+ * Limits: Sk < 2^29, Sq < 2^20, B·Hkv <= 65535.  Returns ATTN_OK (B == 0 or
+ * Sq == 0: nothing launched) or a negative code; checks precede launches.
+ */
+int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_cache, const attn_tensor_t* v_cache,
+                    const int32_t* cache_lens, float scale, int causal, int n_q_heads, int n_kv_heads,
+                    const attn_tensor_t* out, float* lse, void* workspace, int64_t workspace_bytes,
+                    void* stream);
+
+/* Bytes of workspace attn_fwd_decode needs for these sizes: one 256-key chunk
+ * (at least one, also for an empty cache) × B·Hq·Sq rows × (D + 2) floats;
+ * -1 if a size is negative. */
+int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_heads, int64_t D, int64_t Sk);
 
 /* Static, human-readable text for a return code (never NULL). */
 const char* attn_strerror(int code);

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_strerror(lib):
     assert A.version().startswith("attn_fwd ")
     assert "gfx950" in A.version()
-    for code in range(-9, 1):
+    for code in range(-11, 1):
         assert A.strerror(code)
     assert A.strerror(-1234) == "unknown error code"
 
@@ -198,3 +198,42 @@ def test_rope_empty_inputs_return_ok_without_launch(lib):
     assert call_rope(lib, T(**z), T(**z), T(**z), T(**z), T(**z)) == A.ATTN_OK
     z = dict(B=0, data=0)
     assert call_rope(lib, T(**z), T(**z), T(**z), T(**z), T(**z)) == A.ATTN_OK
+
+
+# --------------------------------------------------------------------------
+# attn_fwd_decode / attn_decode_workspace_bytes, host only
+# --------------------------------------------------------------------------
+def call_dec(lib, q, k, v, out, lens=None, causal=1, ws=FAKE + 0x100000, ws_bytes=1 << 30, lse=None):
+    return lib.attn_fwd_decode(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), lens, ctypes.c_float(0.0),
+                               causal, q.H, k.H, ctypes.byref(out), lse, ws, ctypes.c_int64(ws_bytes), None)
+
+
+def test_decode_workspace_bytes(lib):
+    # 256-key chunks x rows x (D + 2) floats
+    assert A.decode_workspace_bytes(2, 1, 64, 128, 4096) == 16 * 2 * 64 * 1 * 130 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 1) == 1 * 1 * 8 * 3 * 66 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 257) == 2 * 1 * 8 * 3 * 66 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 0) == 1 * 1 * 8 * 3 * 66 * 4  # empty cache: one chunk
+    assert lib.attn_decode_workspace_bytes(-1, 1, 1, 64, 1) == -1
+
+
+def test_decode_checks(lib):
+    q, k, v, o = T(S=1, H=8), T(S=100, H=2), T(S=100, H=2), T(S=1, H=8)
+    assert call_dec(lib, q, k, T(S=99, H=2), o) == A.ATTN_ERR_SHAPE          # v length != k length
+    assert call_dec(lib, q, k, v, T(S=2, H=8)) == A.ATTN_ERR_SHAPE           # out rows != q rows
+    assert call_dec(lib, q, T(S=100, H=3), T(S=100, H=3), o) == A.ATTN_ERR_HEADS
+    assert call_dec(lib, q, k, v, o, causal=3) == A.ATTN_ERR_MASK
+    assert call_dec(lib, q, T(S=100, H=2, dtype=A.ATTN_F16), v, o) == A.ATTN_ERR_DTYPE
+    assert call_dec(lib, T(S=1, H=8, D=96), T(S=100, H=2, D=96), T(S=100, H=2, D=96),
+                    T(S=1, H=8, D=96)) == A.ATTN_ERR_UNSUPPORTED
+    assert call_dec(lib, q, k, v, o, lens=FAKE + 2) == A.ATTN_ERR_ALIGN
+    assert call_dec(lib, q, k, v, o, ws=None) == A.ATTN_ERR_NULL
+    need = A.decode_workspace_bytes(1, 1, 8, 64, 100)
+    assert call_dec(lib, q, k, v, o, ws_bytes=need - 1) == A.ATTN_ERR_WORKSPACE
+    assert call_dec(lib, q, k, v, o, ws=FAKE + 0x100008) == A.ATTN_ERR_ALIGN
+
+
+def test_decode_empty_queries_return_ok_without_launch(lib):
+    assert call_dec(lib, T(S=0, H=8), T(S=100, H=2), T(S=100, H=2), T(S=0, H=8)) == A.ATTN_OK
+    assert call_dec(lib, T(B=0, S=1, H=8, data=0), T(B=0, S=5, H=2, data=0), T(B=0, S=5, H=2, data=0),
+                    T(B=0, S=1, H=8, data=0)) == A.ATTN_OK

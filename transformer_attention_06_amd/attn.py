@@ -26,8 +26,10 @@ ATTN_ERR_ALIGN = -7
 ATTN_ERR_LAUNCH = -8
 ATTN_ERR_DEVICE = -9
 ATTN_ERR_ALIAS = -10
+ATTN_ERR_WORKSPACE = -11
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_rope", "attn_strerror", "attn_version")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_rope", "attn_fwd_decode", "attn_decode_workspace_bytes",
+                    "attn_strerror", "attn_version")
 
 
 class AttnTensor(ctypes.Structure):
@@ -64,6 +66,13 @@ def load_library(path=LIB_PATH):
                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, P, P,
                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_fwd_rope.restype = ctypes.c_int
+    lib.attn_fwd_decode.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_void_p]
+    lib.attn_fwd_decode.restype = ctypes.c_int
+    lib.attn_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
+                                                ctypes.c_int64]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_int64
     lib.attn_strerror.argtypes = [ctypes.c_int]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -221,3 +230,57 @@ def rope_attention(q, k, v, *, causal=False, pad_lens=None, scale=None, position
     attn_fwd_rope(q, k, v, mask_kind, pad_lens, scale, causal, q.shape[2], k.shape[2], positions, rope_base,
                   k_rot, out, lse)
     return (out, k_rot, lse) if return_lse else (out, k_rot)
+
+
+def decode_workspace_bytes(B, Sq, n_q_heads, D, Sk):
+    """Bytes of workspace attn_fwd_decode needs."""
+    return int(load_library().attn_decode_workspace_bytes(int(B), int(Sq), int(n_q_heads), int(D), int(Sk)))
+
+
+def attn_fwd_decode(q, k_cache, v_cache, cache_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
+                    workspace, stream=None):
+    """``attn_fwd_decode`` with torch tensors: q/out (B, Sq, Hq, D), caches
+    (B, Sk, Hkv, D), cache_lens int32 [B] or None, workspace a uint8 device
+    tensor of at least decode_workspace_bytes(...) bytes."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("workspace", workspace)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    lens_ptr = None
+    if cache_lens is not None:
+        if cache_lens.dtype != torch.int32 or not cache_lens.is_cuda or not cache_lens.is_contiguous():
+            raise ValueError("cache_lens must be a contiguous int32 device tensor")
+        lens_ptr = ctypes.c_void_p(cache_lens.data_ptr())
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 device tensor")
+        if tuple(lse.shape) != (q.shape[0], n_q_heads, q.shape[1]):
+            raise ValueError("lse must be [B, n_q_heads, Sq]")
+        lse_ptr = ctypes.c_void_p(lse.data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    dq, dk, dv, do = describe(q), describe(k_cache), describe(v_cache), describe(out)
+    code = lib.attn_fwd_decode(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), lens_ptr,
+                               ctypes.c_float(0.0 if scale is None else float(scale)), int(bool(causal)),
+                               int(n_q_heads), int(n_kv_heads), ctypes.byref(do), lse_ptr,
+                               ctypes.c_void_p(workspace.data_ptr()),
+                               ctypes.c_int64(workspace.numel() * workspace.element_size()),
+                               ctypes.c_void_p(stream.cuda_stream))
+    check(code)
+    return out, lse
+
+
+def decode_attention(q, k_cache, v_cache, *, cache_lens=None, causal=True, scale=None, return_lse=False):
+    """Allocate ``out``, the workspace (and ``lse``) with torch and run
+    ``attn_fwd_decode``.  Returns out, or (out, lse)."""
+    import torch
+    B, Sq, Hq, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    ws = torch.empty(max(16, decode_workspace_bytes(B, Sq, Hq, D, k_cache.shape[1])), dtype=torch.uint8,
+                     device=q.device)
+    attn_fwd_decode(q, k_cache, v_cache, cache_lens, scale, causal, Hq, k_cache.shape[2], out, lse, ws)
+    return (out, lse) if return_lse else out
+

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_fwd.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", "attn_decode_kernels.hip"]
 
 # Packed-fp32 VALU forms are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -30,33 +30,39 @@ def hipcc():
 
 
 def build(verbose=False, extra_flags=()):
-    """Compile every source into LIB; returns the library path.  The device
-    assembly of the kernels is compiled alongside and checked for MFMA wait
-    states (asm_check); the library is only installed if that check passes."""
+    """Compile every source into LIB; returns the library path.  The sources
+    compile to objects in parallel; the device assembly of the attention
+    kernels is compiled alongside and checked for MFMA wait states
+    (asm_check); the library is only installed if that check passes."""
     tmp = LIB + ".tmp"
     common = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
               *DEVICE_FLAGS, *extra_flags]
-    cmd = [hipcc(), *common, "-shared", "-Wall", "-Wno-unused-result", "-Wno-pass-failed", "-o", tmp]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
     with tempfile.TemporaryDirectory() as td:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(td, os.path.splitext(src)[0] + ".o")
+            objs.append(obj)
+            cmd = [hipcc(), *common, "-c", "-Wall", "-Wno-unused-result", "-Wno-pass-failed", "-o", obj,
+                   os.path.join(CSRC, src)]
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
         asm = os.path.join(td, "kernels.s")
-        acmd = [hipcc(), *common, "--cuda-device-only", "-S", "-o", asm,
+        acmd = [hipcc(), *common, "--cuda-device-only", "-S", "-Wno-pass-failed", "-o", asm,
                 os.path.join(CSRC, "attn_fwd_kernels.hip")]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-            print(" ".join(acmd), flush=True)
-        lib_p = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
-        asm_p = subprocess.Popen(acmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
-        out, err = lib_p.communicate()
-        aout, aerr = asm_p.communicate()
-        if lib_p.returncode != 0:
-            sys.stderr.write(out + err)
-            raise RuntimeError(f"hipcc failed with exit code {lib_p.returncode}")
-        if asm_p.returncode != 0:
-            sys.stderr.write(aout + aerr)
-            raise RuntimeError(f"hipcc (device assembly) failed with exit code {asm_p.returncode}")
-        if verbose and (out or err):
-            sys.stderr.write(out + err)
+        procs.append((acmd, subprocess.Popen(acmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        for cmd, pr in procs:
+            out, err = pr.communicate()
+            if verbose:
+                print(" ".join(cmd), flush=True)
+                if out or err:
+                    sys.stderr.write(out + err)
+            if pr.returncode != 0:
+                sys.stderr.write(out + err)
+                raise RuntimeError(f"hipcc failed with exit code {pr.returncode}: {' '.join(cmd[-1:])}")
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        lk = subprocess.run(link, capture_output=True, text=True)
+        if lk.returncode != 0:
+            sys.stderr.write(lk.stdout + lk.stderr)
+            raise RuntimeError(f"link failed with exit code {lk.returncode}")
         sys.path.insert(0, PKG)
         try:
             import asm_check

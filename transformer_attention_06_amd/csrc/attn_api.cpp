@@ -165,6 +165,79 @@ extern "C" int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, con
     return attn_detail::launch(a);
 }
 
+// Decode attention over a KV cache: Sq new rows per sequence against the
+// first cache_lens[b] cached rows, end-aligned causal rule (the ATB
+// introduction's FlashAttention with KV-cache management; "CANN-ops-
+// transformer和ATB…" passes the cache into FlashAttention every step).
+extern "C" int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_heads, int64_t D, int64_t Sk) {
+    if (B < 0 || Sq < 0 || n_q_heads < 0 || D < 0 || Sk < 0) return -1;
+    const int64_t rows = B * int64_t(n_q_heads) * Sq;
+    const int64_t n_split = attn_detail::decode_splits(Sk);
+    return n_split * rows * (D + 2) * int64_t(sizeof(float));
+}
+
+extern "C" int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_cache,
+                               const attn_tensor_t* v_cache, const int32_t* cache_lens, float scale,
+                               int causal, int n_q_heads, int n_kv_heads, const attn_tensor_t* out,
+                               float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!q || !k_cache || !v_cache || !out) return ATTN_ERR_NULL;
+    const attn_tensor_t* all[4] = {q, k_cache, v_cache, out};
+    for (const attn_tensor_t* t : all)
+        if (!valid_dtype(t->dtype)) return ATTN_ERR_DTYPE;
+    for (const attn_tensor_t* t : all)
+        if (t->dtype != q->dtype) return ATTN_ERR_DTYPE;
+    for (const attn_tensor_t* t : all)
+        if (t->B < 0 || t->S < 0 || t->H < 0 || t->D < 0) return ATTN_ERR_SHAPE;
+    if (k_cache->B != q->B || v_cache->B != q->B || out->B != q->B) return ATTN_ERR_SHAPE;
+    if (k_cache->D != q->D || v_cache->D != q->D || out->D != q->D) return ATTN_ERR_SHAPE;
+    if (v_cache->S != k_cache->S || out->S != q->S) return ATTN_ERR_SHAPE;
+    if (n_q_heads <= 0 || n_kv_heads <= 0) return ATTN_ERR_HEADS;
+    if (q->H != n_q_heads || out->H != n_q_heads) return ATTN_ERR_HEADS;
+    if (k_cache->H != n_kv_heads || v_cache->H != n_kv_heads) return ATTN_ERR_HEADS;
+    if (n_q_heads % n_kv_heads != 0 || n_q_heads > 65535) return n_q_heads > 65535 ? ATTN_ERR_UNSUPPORTED
+                                                                                    : ATTN_ERR_HEADS;
+    if (causal != 0 && causal != 1) return ATTN_ERR_MASK;
+    if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u) != 0) return ATTN_ERR_ALIGN;
+    if (q->D != 64 && q->D != 128) return ATTN_ERR_UNSUPPORTED;
+    const int64_t B = q->B, Sq = q->S, Sk = k_cache->S, D = q->D;
+    if (B == 0 || Sq == 0) return ATTN_OK;  // no query row: nothing to launch
+    if (Sk >= (int64_t(1) << 29) || Sq >= (int64_t(1) << 20)) return ATTN_ERR_UNSUPPORTED;
+    if (B > 65535 || B * n_kv_heads > 65535) return ATTN_ERR_UNSUPPORTED;
+    const int64_t rows_per_kv = int64_t(n_q_heads / n_kv_heads) * Sq;
+    if ((rows_per_kv + 7) / 8 > 65535) return ATTN_ERR_UNSUPPORTED;
+    const int64_t need = attn_decode_workspace_bytes(B, Sq, n_q_heads, D, Sk);
+    if (!q->data || !out->data) return ATTN_ERR_NULL;
+    if (Sk > 0 && (!k_cache->data || !v_cache->data)) return ATTN_ERR_NULL;
+    if (!workspace) return ATTN_ERR_NULL;
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(q->data) || !aligned16(out->data) || !aligned16(workspace) ||
+        (Sk > 0 && (!aligned16(k_cache->data) || !aligned16(v_cache->data))))
+        return ATTN_ERR_ALIGN;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
+    float sc = scale;
+    if (!(sc > 0.0f) || !std::isfinite(sc)) sc = 1.0f / std::sqrt(float(D));
+    attn_detail::DecodeArgs a;
+    a.q = q->data;
+    a.k = k_cache->data;
+    a.v = v_cache->data;
+    a.o = out->data;
+    a.lse = lse;
+    a.cache_lens = cache_lens;
+    a.workspace = workspace;
+    a.dtype = q->dtype;
+    a.B = B;
+    a.Sq = Sq;
+    a.Sk = Sk;
+    a.Hq = n_q_heads;
+    a.Hkv = n_kv_heads;
+    a.D = D;
+    a.causal = causal;
+    a.n_split = attn_detail::decode_splits(Sk);
+    a.scale = sc;
+    a.stream = stream;
+    return attn_detail::launch_decode(a);
+}
+
 extern "C" const char* attn_strerror(int code) {
     switch (code) {
         case ATTN_OK: return "success";
@@ -178,6 +251,7 @@ extern "C" const char* attn_strerror(int code) {
         case ATTN_ERR_LAUNCH: return "the HIP kernel launch failed";
         case ATTN_ERR_DEVICE: return "the current device cannot run this library's gfx950 code";
         case ATTN_ERR_ALIAS: return "k_rot overlaps q, v, out, lse, or part of k (it may be k itself)";
+        case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes() requires";
         default: return "unknown error code";
     }
 }

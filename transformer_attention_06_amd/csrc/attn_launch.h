@@ -37,4 +37,27 @@ int launch(const LaunchArgs& a);
 // k_out (same layout; may be a.k itself) with a.rope_pos and a.rope_f.
 int launch_rope_k(const LaunchArgs& a, void* k_out);
 
+// Decode attention over a KV cache (split over key chunks, then merged).
+struct DecodeArgs {
+    const void* q;             // (B, Sq, Hq, D)
+    const void* k;             // (B, Sk, Hkv, D)
+    const void* v;
+    void* o;                   // (B, Sq, Hq, D)
+    float* lse;                // (B, Hq, Sq) or null
+    const int32_t* cache_lens; // int32[B] or null (= Sk)
+    void* workspace;           // decode_workspace_bytes(...) bytes, 16-byte aligned
+    int32_t dtype;
+    int64_t B, Sq, Sk, Hq, Hkv, D;
+    int causal;
+    int n_split;
+    float scale;
+    void* stream;
+};
+
+// Key chunks a cache of Sk rows is split into.
+int decode_splits(int64_t Sk);
+
+// Enqueue the split and merge kernels.
+int launch_decode(const DecodeArgs& a);
+
 }  // namespace attn_detail
