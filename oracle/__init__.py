@@ -25,7 +25,11 @@ The rotary embedding (``rope``) is pinned the same way by
 invariants, the relative-position property and the complex-number form), and
 decode attention over a KV cache (``attention_decode``) by
 ``tests/oracle_decode_pins.py`` (equality with the last rows of a prefill,
-cache truncation, the key-split merge by LSE, torch's SDPA).
+cache truncation, the key-split merge by LSE, torch's SDPA), and attention over packed
+variable-length sequences (``attention_varlen``) by
+``tests/oracle_varlen_pins.py`` (the batched oracle at equal lengths, key
+padding standing in for a shorter sequence, torch's SDPA per sequence, the
+uniform-score closed form, independence of sequences).
 """
 
 from .attention import (  # noqa: F401
@@ -47,4 +51,8 @@ from .rope import (  # noqa: F401
 from .decode import (  # noqa: F401
     visible_keys as decode_visible_keys,
     attention_decode,
+)
+from .varlen import (  # noqa: F401
+    check_offsets as varlen_check_offsets,
+    attention_varlen,
 )

@@ -155,3 +155,59 @@ def test_decode_mutant_is_caught(name):
         except (AssertionError, FloatingPointError, ValueError, IndexError):
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+# --------------------------------------------------------------------------
+# packed variable-length attention (oracle/varlen.py) against
+# tests/oracle_varlen_pins.py
+# --------------------------------------------------------------------------
+import oracle_varlen_pins  # noqa: E402
+
+VARLEN_SRC = os.path.join(os.path.dirname(oracle.__file__), "varlen.py")
+
+VARLEN_MUTANTS = {
+    "end_off_by_one": ("s0, s1 = int(cu[b]), int(cu[b + 1])", "s0, s1 = int(cu[b]), int(cu[b + 1]) + 1"),
+    "start_off_by_one": ("s0, s1 = int(cu[b]), int(cu[b + 1])", "s0, s1 = max(int(cu[b]) - 1, 0), int(cu[b + 1])"),
+    "causal_strict": ("visible = (j_loc <= i_loc) if causal", "visible = (j_loc < i_loc) if causal"),
+    "causal_wrong_direction": ("visible = (j_loc <= i_loc) if causal", "visible = (j_loc >= i_loc) if causal"),
+    "causal_ignored": ("visible = (j_loc <= i_loc) if causal", "visible = (j_loc <= i_loc) if False"),
+    "gqa_interleaved": ("g = (h * hkv) // hq", "g = h % hkv"),
+    "dropped_scale": ("scores = (q[s0:s1, h, :] @ k[s0:s1, g, :].T) * scale",
+                      "scores = (q[s0:s1, h, :] @ k[s0:s1, g, :].T)"),
+    "transposed_scores": ("scores = (q[s0:s1, h, :] @ k[s0:s1, g, :].T) * scale",
+                          "scores = (k[s0:s1, g, :] @ q[s0:s1, h, :].T) * scale"),
+    "unnormalised": ("out[s0:s1, h, :] = (e / den[:, None]) @ v[s0:s1, g, :]",
+                     "out[s0:s1, h, :] = e @ v[s0:s1, g, :]"),
+    "v_from_query_head": ("out[s0:s1, h, :] = (e / den[:, None]) @ v[s0:s1, g, :]",
+                          "out[s0:s1, h, :] = (e / den[:, None]) @ v[s0:s1, h % hkv, :]"),
+    "lse_missing_max": ("lse[h, s0:s1] = m + np.log(den)", "lse[h, s0:s1] = np.log(den)"),
+    "default_scale_1_over_d": ("scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d"),
+    "offsets_unchecked": ("    if np.any(np.diff(cu) < 0) or cu[0] < 0 or cu[-1] > total:",
+                          "    if False:"),
+}
+
+
+def _load_varlen_mutant(find, repl):
+    src = open(VARLEN_SRC).read()
+    assert src.count(find) == 1, f"mutation anchor not unique/found: {find!r}"
+    mod = types.ModuleType("oracle_varlen_mutant")
+    exec(compile(src.replace(find, repl), "oracle_varlen_mutant.py", "exec"), mod.__dict__)
+    # the pins also use the (pinned) prefill oracle through the same module
+    mod.attention = oracle.attention
+    mod.MASK_KEY_PADDING = oracle.MASK_KEY_PADDING
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_MUTANTS))
+def test_varlen_mutant_is_caught(name):
+    mod = _load_varlen_mutant(*VARLEN_MUTANTS[name])
+    caught = []
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        for pin in oracle_varlen_pins.ALL_PINS:
+            try:
+                pin(mod)
+            except (AssertionError, FloatingPointError, ValueError, IndexError):
+                caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"

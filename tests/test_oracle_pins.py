@@ -21,3 +21,11 @@ def test_rope_pin(pin):
 @pytest.mark.parametrize("pin", oracle_decode_pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_decode_pin(pin):
     pin(oracle)
+
+
+import oracle_varlen_pins  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", oracle_varlen_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_varlen_pin(pin):
+    pin(oracle)
