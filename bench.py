@@ -15,7 +15,8 @@ kernel source, else null.  The cpu_baseline block times the fp64 CPU oracle on
 a bounded sample of heads of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--all] [--sweep] [--rope] [--decode] [--copy-calibration]
+                    [--no-cpu-baseline] [--all] [--sweep] [--rope] [--decode] [--varlen]
+                    [--copy-calibration]
 """
 
 import argparse
@@ -50,6 +51,52 @@ def min_hbm_bytes(w, pad):
     return qo + kv + lse
 
 
+def time_steps(step, steps, warmup, use_graph=True, warmup_s=0.0):
+    """Run ``step`` (which launches on the current stream) for an untimed
+    warmup of at least ``warmup`` steps and ``warmup_s`` seconds, then time
+    exactly ``steps`` steps: captured once as a HIP graph and replayed (or
+    launched eagerly), bracketed by HIP events on the launch stream (device
+    time per step) and by synchronize + a host clock (wall time per step).
+    Returns (wall ms per step, device ms per step, warmup steps done)."""
+    import torch
+    t_w = time.perf_counter()
+    done = 0
+    while done < warmup or (warmup_s > 0 and time.perf_counter() - t_w < warmup_s):
+        step()
+        done += 1
+        if done % 20 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                step()
+        graph.replay()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(steps):
+            step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps, done
+
+
 def run_gpu(w, steps, warmup, use_graph=True, warmup_s=0.0, rope=False):
     import torch
     from transformer_attention_06_amd import attn as A
@@ -73,52 +120,8 @@ def run_gpu(w, steps, warmup, use_graph=True, warmup_s=0.0, rope=False):
         else:
             A.attn_fwd(qd, kd, vd, mask, pad_d, None, w.causal, w.Hq, w.Hkv, out, lse)
 
-    # Untimed warmup: at least `warmup` steps, and (by default) at least half
-    # a second of them, so the timed region starts at a settled clock.
-    t_w = time.perf_counter()
-    done = 0
-    while done < warmup or (warmup_s > 0 and time.perf_counter() - t_w < warmup_s):
-        step()
-        done += 1
-        if done % 20 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-
-    graph = None
-    if use_graph:
-        # The K timed steps are captured once as a HIP graph and replayed, so
-        # the device runs them back to back without host launch gaps.
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        with torch.cuda.graph(graph):
-            for _ in range(steps):
-                step()
-        graph.replay()
-        torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-
-    # Timed region: K steps on the launch stream, bracketed by HIP events on
-    # that stream (device time per launch) and by synchronize + a host clock
-    # (wall time, the reported throughput).
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for _ in range(steps):
-            step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    dev_ms = e0.elapsed_time(e1)
-    return dict(ms_per_step=(t1 - t0) * 1e3 / steps, kernel_ms_mean=dev_ms / steps, pad=pad, warmup_done=done)
+    ms_wall, ms_dev, done = time_steps(step, steps, warmup, use_graph, warmup_s)
+    return dict(ms_per_step=ms_wall, kernel_ms_mean=ms_dev, pad=pad, warmup_done=done)
 
 
 KERNEL_SOURCES = ["transformer_attention_06_amd/csrc/attn_fwd_kernels.hip",
@@ -219,41 +222,7 @@ def bench_decode(name, steps, warmup, use_graph=True, warmup_s=0.0):
     def step():
         A.attn_fwd_decode(q, k, v, None, None, True, Hq, Hkv, out, lse, ws)
 
-    t_w = time.perf_counter()
-    done = 0
-    while done < warmup or (warmup_s > 0 and time.perf_counter() - t_w < warmup_s):
-        step()
-        done += 1
-    torch.cuda.synchronize()
-    graph = None
-    if use_graph:
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        with torch.cuda.graph(graph):
-            for _ in range(steps):
-                step()
-        graph.replay()
-        torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for _ in range(steps):
-            step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_wall = (t1 - t0) * 1e3 / steps
-    ms_dev = e0.elapsed_time(e1) / steps
+    ms_wall, ms_dev, done = time_steps(step, steps, warmup, use_graph, warmup_s)
     nbytes = 2 * B * Sk * Hkv * D * 2 + 2 * B * Sq * Hq * D * 2 + B * Hq * Sq * 4
     gbs = nbytes / (ms_wall * 1e-3) / 1e9
     achieved = nbytes / (ms_dev * 1e-3) / 1e9
@@ -267,6 +236,64 @@ def bench_decode(name, steps, warmup, use_graph=True, warmup_s=0.0):
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                          "call_us_mean": round(ms_dev * 1e3, 3), "algorithmic_bytes_per_call": nbytes,
                          "workspace_bytes": int(ws.numel())}}
+
+
+def bench_varlen(steps, warmup, use_graph=True, warmup_s=0.0, name="batched_varlen"):
+    """Packed variable-length sequences (attn_fwd_varlen): the batched short
+    sequences (16 lengths in [128, 512], 32 heads, D = 64, fp16, non-causal)
+    packed with no padding.  The FLOP count is the algorithmic one, Σ_b
+    4·H·L_b²·D (no padded row or key exists); the same lengths run through
+    attn_fwd's key-padding path (B × 512 rows, padded query rows computed)
+    in the same process give the cost of padding."""
+    import torch
+    from transformer_attention_06_amd import attn as A
+    from transformer_attention_06_amd import workloads as W
+    w = W.WORKLOADS[name]
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    q, k, v, cu = W.make_varlen_inputs(w)
+    lens = np.diff(cu)
+    qd, kd, vd = (torch.from_numpy(x).to(dt).cuda() for x in (q, k, v))
+    cu_d = torch.from_numpy(cu.astype(np.int32)).cuda()
+    out = torch.empty_like(qd)
+    max_len = int(lens.max())
+
+    def step():
+        A.attn_fwd_varlen(qd, kd, vd, cu_d, max_len, None, w.causal, w.Hq, w.Hkv, out, None)
+
+    ms_wall, ms_dev, done = time_steps(step, steps, warmup, use_graph, warmup_s)
+    # the same sequences padded to S = 512 under key padding
+    pq, pk, pv = (torch.zeros((w.B, w.S) + x.shape[1:], dtype=dt, device="cuda") for x in (q, k, v))
+    for b in range(w.B):
+        pq[b, :lens[b]], pk[b, :lens[b]], pv[b, :lens[b]] = qd[cu[b]:cu[b + 1]], kd[cu[b]:cu[b + 1]], vd[cu[b]:cu[b + 1]]
+    pad_d = torch.from_numpy(lens.astype(np.int32)).cuda()
+    pout = torch.empty_like(pq)
+
+    def step_pad():
+        A.attn_fwd(pq, pk, pv, A.ATTN_MASK_KEY_PADDING, pad_d, None, w.causal, w.Hq, w.Hkv, pout, None)
+
+    _, ms_pad, _ = time_steps(step_pad, steps, warmup, use_graph, warmup_s)
+    fl = float(sum(4.0 * w.Hq * float(L) ** 2 * w.D for L in lens))
+    if w.causal:
+        fl /= 2.0
+    el = {"bf16": 2, "fp16": 2, "fp32": 4}[w.dtype]
+    nbytes = int(cu[-1]) * (2 * w.Hq + 2 * w.Hkv) * w.D * el
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = fl / (ms_dev * 1e-3) / 1e12
+    return {"metric": "packed variable-length attention: algorithmic TFLOP/s", "value": round(fl / (ms_wall * 1e-3) / 1e12, 3),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": done, "ms_per_step": round(ms_wall, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic (seeded lengths in [128, 512], N(0,1) Q, K, V)",
+            "config": {"workload": name, "B": w.B, "T": int(cu[-1]), "max_seqlen": max_len, "Hq": w.Hq,
+                       "Hkv": w.Hkv, "D": w.D, "causal": w.causal,
+                       "timing": "hip_graph_replay" if use_graph else "eager_launches"},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(achieved / peak, 4), "traffic": None,
+                         "kernel_us_mean": round(ms_dev * 1e3, 3), "flops_per_launch": fl,
+                         "min_hbm_bytes_per_launch": nbytes,
+                         "hbm_frac": round(nbytes / (ms_dev * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "padded": {"kernel_us_mean": round(ms_pad * 1e3, 3),
+                       "algorithmic_tflops": round(fl / (ms_pad * 1e-3) / 1e12, 3),
+                       "note": "same sequences through attn_fwd key padding at S = 512"}}
 
 
 def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0, rope=False):
@@ -340,6 +367,8 @@ def main():
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
     ap.add_argument("--decode", action="store_true",
                     help="decode attention over a KV cache (attn_fwd_decode), Llama-2-70B shapes, HBM roofline")
+    ap.add_argument("--varlen", action="store_true",
+                    help="packed variable-length sequences (attn_fwd_varlen) vs the same lengths padded")
     ap.add_argument("--rope", action="store_true",
                     help="time attn_fwd_rope (rotary embedding of Q and K fused with the attention)")
     ap.add_argument("--sweep", action="store_true",
@@ -364,6 +393,9 @@ def main():
         for name in DECODE_SHAPES:
             print(json.dumps(bench_decode(name, args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)
         return
+    if args.varlen:
+        print(json.dumps(bench_varlen(args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)
+        return
     if args.sweep:
         from transformer_attention_06_amd import workloads as W
         base = None
@@ -380,6 +412,8 @@ def main():
     if args.all:
         from transformer_attention_06_amd import workloads as W
         for name in W.WORKLOADS:
+            if name == "batched_varlen":  # packed inputs: --varlen
+                continue
             print(json.dumps(bench_one(name, args.steps, args.warmup, False, not args.no_graph, warmup_s)), flush=True)
         print(json.dumps(bench_one(DEFAULT_WORKLOAD, args.steps, args.warmup, False, not args.no_graph, warmup_s,
                                    rope=True)), flush=True)

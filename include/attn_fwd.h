@@ -120,6 +120,45 @@ int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t
              const attn_tensor_t* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_varlen — attn_fwd over packed sequences of different lengths.
+ *
+ * The ATB engineering guide (hwcomputing.csdn.net/6a59a88310ee7a33f28e5ce9)
+ * §6.1 has the attention operator adapt at run time to sequence lengths that
+ * vary per request (32 to 4096 tokens), and its §8.7 drives one MhaV3
+ * operator over such lengths; "ops-transformer：Transformer算子融合与推理加速
+ * 实战" §5.2 merges batch and heads into one parallel axis and then splits
+ * the sequence.  Here a batch of such sequences is packed back to back with
+ * no padding: sequence b is rows [cu_seqlens[b], cu_seqlens[b+1]) of
+ *
+ *   q, out: (1, T, Hq, D);  k, v: (1, T, Hkv, D)
+ *
+ * and each sequence is an independent self-attention over its own rows,
+ * computed as attn_fwd documents (scale, GQA mapping, LSE definition), with
+ * the causal rule counted within the sequence (key j visible to query i iff
+ * j <= i, both counted from the sequence's first row).  No padded row is
+ * computed and no padded key is read.
+ *
+ *   cu_seqlens  device int32[n_seqs + 1] (4-byte aligned), non-decreasing,
+ *               within [0, T].  Offsets are clamped into [0, T] on the
+ *               device (so a bad offset cannot leave the buffers).
+ *   n_seqs      number of sequences B (>= 0).
+ *   max_seqlen  an upper bound on every length, 0 <= max_seqlen <= T (else
+ *               ATTN_ERR_SHAPE); it sizes the launch.  A longer sequence is
+ *               treated as its first max_seqlen rows.
+ *   out         rows inside a sequence are written; rows outside every
+ *               sequence are left untouched.
+ *   lse         device float[Hq, T] (row r of head h at h*T + r), or NULL.
+ *   q, k, v, scale, causal, n_q_heads, n_kv_heads, stream: as for attn_fwd
+ *               (descriptors with B == 1, S == T; else ATTN_ERR_SHAPE).
+ *
+ * Limits: as for attn_fwd with S = T.  n_seqs == 0, T == 0 or
+ * max_seqlen == 0: ATTN_OK, nothing launched.  All checks precede the launch.
+ */
+int attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                    const int32_t* cu_seqlens, int n_seqs, int64_t max_seqlen, float scale, int causal,
+                    int n_q_heads, int n_kv_heads, const attn_tensor_t* out, float* lse, void* stream);
+
+/*
  * attn_fwd_rope — rotary position embedding of Q and K fused with attn_fwd.
  *
  * The fifth fusion pattern of the ATB engineering guide
@@ -186,8 +225,11 @@ int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, const attn_ten
  *               must not overlap.
  *
  * Two launches on `stream`: one workgroup per (256-key chunk, batch, kv head,
- * 8 query rows) writes the chunk's partial (O, max, sum); a merge kernel
- * combines the chunks by their log-sum-exp and writes O and LSE.
+ * 32 query rows; 8 for fp32) writes the chunk's partial (O, max, sums); a
+ * merge kernel combines the chunks by their log-sum-exp and writes O and LSE.
+ * bf16/fp16 run both products on MFMA with fp32 accumulation, P rounded to
+ * the input type, O normalised by the sum of the rounded probabilities and
+ * LSE taken from the exact sum.
  * Limits: Sk < 2^29, Sq < 2^20, B·Hkv <= 65535.  Returns ATTN_OK (B == 0 or
  * Sq == 0: nothing launched) or a negative code; checks precede launches.
  */
@@ -197,7 +239,7 @@ int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_cache, const 
                     void* stream);
 
 /* Bytes of workspace attn_fwd_decode needs for these sizes: one 256-key chunk
- * (at least one, also for an empty cache) × B·Hq·Sq rows × (D + 2) floats;
+ * (at least one, also for an empty cache) × B·Hq·Sq rows × (D + 3) floats;
  * -1 if a size is negative. */
 int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_heads, int64_t D, int64_t Sk);
 

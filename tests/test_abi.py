@@ -209,11 +209,11 @@ def call_dec(lib, q, k, v, out, lens=None, causal=1, ws=FAKE + 0x100000, ws_byte
 
 
 def test_decode_workspace_bytes(lib):
-    # 256-key chunks x rows x (D + 2) floats
-    assert A.decode_workspace_bytes(2, 1, 64, 128, 4096) == 16 * 2 * 64 * 1 * 130 * 4
-    assert A.decode_workspace_bytes(1, 3, 8, 64, 1) == 1 * 1 * 8 * 3 * 66 * 4
-    assert A.decode_workspace_bytes(1, 3, 8, 64, 257) == 2 * 1 * 8 * 3 * 66 * 4
-    assert A.decode_workspace_bytes(1, 3, 8, 64, 0) == 1 * 1 * 8 * 3 * 66 * 4  # empty cache: one chunk
+    # 256-key chunks x rows x (D + 3) floats
+    assert A.decode_workspace_bytes(2, 1, 64, 128, 4096) == 16 * 2 * 64 * 1 * 131 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 1) == 1 * 1 * 8 * 3 * 67 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 257) == 2 * 1 * 8 * 3 * 67 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 0) == 1 * 1 * 8 * 3 * 67 * 4  # empty cache: one chunk
     assert lib.attn_decode_workspace_bytes(-1, 1, 1, 64, 1) == -1
 
 
@@ -237,3 +237,36 @@ def test_decode_empty_queries_return_ok_without_launch(lib):
     assert call_dec(lib, T(S=0, H=8), T(S=100, H=2), T(S=100, H=2), T(S=0, H=8)) == A.ATTN_OK
     assert call_dec(lib, T(B=0, S=1, H=8, data=0), T(B=0, S=5, H=2, data=0), T(B=0, S=5, H=2, data=0),
                     T(B=0, S=1, H=8, data=0)) == A.ATTN_OK
+
+
+# --------------------------------------------------------------------------
+# attn_fwd_varlen: packed (1, T, H, D) buffers with offsets, host only
+# --------------------------------------------------------------------------
+def call_var(lib, q, k, v, out, cu=FAKE + 0x200000, n=3, max_len=8, causal=0, lse=None):
+    return lib.attn_fwd_varlen(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), cu, n, ctypes.c_int64(max_len),
+                               ctypes.c_float(0.0), causal, q.H, k.H, ctypes.byref(out), lse, None)
+
+
+def test_varlen_checks(lib):
+    q, k, v, o = T(S=20, H=4), T(S=20, H=2), T(S=20, H=2), T(S=20, H=4)
+    assert call_var(lib, T(B=2, S=20, H=4), T(B=2, S=20, H=2), T(B=2, S=20, H=2),
+                    T(B=2, S=20, H=4)) == A.ATTN_ERR_SHAPE                  # packed buffers have B == 1
+    assert call_var(lib, q, k, T(S=19, H=2), o) == A.ATTN_ERR_SHAPE         # v rows != T
+    assert call_var(lib, q, k, v, o, max_len=21) == A.ATTN_ERR_SHAPE         # longer than T
+    assert call_var(lib, q, k, v, o, max_len=-1) == A.ATTN_ERR_SHAPE
+    assert call_var(lib, q, k, v, o, n=-1) == A.ATTN_ERR_SHAPE
+    assert call_var(lib, q, k, v, o, cu=None) == A.ATTN_ERR_NULL
+    assert call_var(lib, q, k, v, o, cu=FAKE + 2) == A.ATTN_ERR_ALIGN
+    assert call_var(lib, q, T(S=20, H=3), T(S=20, H=3), o) == A.ATTN_ERR_HEADS
+    assert call_var(lib, q, k, v, o, causal=2) == A.ATTN_ERR_MASK
+    assert call_var(lib, T(S=20, H=4, D=96), T(S=20, H=2, D=96), T(S=20, H=2, D=96),
+                    T(S=20, H=4, D=96)) == A.ATTN_ERR_UNSUPPORTED
+    assert call_var(lib, q, k, v, o, lse=FAKE + 2) == A.ATTN_ERR_ALIGN
+
+
+def test_varlen_empty_returns_ok_without_launch(lib):
+    q, k, v, o = T(S=20, H=4), T(S=20, H=2), T(S=20, H=2), T(S=20, H=4)
+    assert call_var(lib, q, k, v, o, n=0) == A.ATTN_OK
+    assert call_var(lib, q, k, v, o, max_len=0) == A.ATTN_OK
+    z = dict(S=0, data=0)
+    assert call_var(lib, T(H=4, **z), T(H=2, **z), T(H=2, **z), T(H=4, **z), max_len=0) == A.ATTN_OK

@@ -1,8 +1,8 @@
 """attn_fwd_decode (split-KV decode attention over a KV cache) vs the fp64
 decode oracle, through the C ABI.
 
-Cases cover one and several new rows per sequence (several query-row groups
-per workgroup), MHA/GQA/MQA groupings, cache lengths that end inside a
+Cases cover one and several new rows per sequence (up to 64 rows per kv head,
+i.e. several query-row groups), MHA/GQA/MQA groupings, cache lengths that end inside a
 256-key chunk, are shorter than the number of new rows (rows that see no
 key), are zero, and an empty cache; every dtype and head dimension.
 """
@@ -46,6 +46,10 @@ CASES = [
     (6, 1, 1, 256, 32, 32, 128, "bf16", True, None),          # one full chunk
     (7, 2, 2, 1500, 16, 2, 64, "bf16", True, [1499, 256]),
     (8, 1, 2, 333, 8, 8, 128, "fp32", True, None),
+    (14, 1, 3, 900, 16, 1, 64, "fp16", True, [899]),         # 48 rows per kv head: two row groups
+    (15, 2, 1, 3000, 64, 1, 128, "bf16", True, [3000, 1234]), # MQA, 64 rows per kv head
+    (16, 1, 1, 20000, 8, 2, 128, "bf16", True, None),        # 79 key chunks: merge past 64 chunks
+    (17, 1, 2, 17000, 4, 4, 64, "fp16", False, [16900]),     # 67 chunks, non-causal
 ]
 
 

@@ -28,8 +28,8 @@ ATTN_ERR_DEVICE = -9
 ATTN_ERR_ALIAS = -10
 ATTN_ERR_WORKSPACE = -11
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_rope", "attn_fwd_decode", "attn_decode_workspace_bytes",
-                    "attn_strerror", "attn_version")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_rope", "attn_fwd_decode",
+                    "attn_decode_workspace_bytes", "attn_strerror", "attn_version")
 
 
 class AttnTensor(ctypes.Structure):
@@ -62,6 +62,9 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
                              ctypes.c_int, ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_varlen.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd_varlen.restype = ctypes.c_int
     lib.attn_fwd_rope.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, P, P,
                                   ctypes.c_void_p, ctypes.c_void_p]
@@ -213,6 +216,59 @@ def flash_attention(q, k, v, *, causal=False, pad_lens=None, scale=None, return_
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
     mask_kind = ATTN_MASK_NONE if pad_lens is None else ATTN_MASK_KEY_PADDING
     attn_fwd(q, k, v, mask_kind, pad_lens, scale, causal, q.shape[2], k.shape[2], out, lse)
+    return (out, lse) if return_lse else out
+
+
+def describe_packed(t):
+    """AttnTensor (B = 1, S = T) for a contiguous 3-D (T, H, D) torch tensor."""
+    if t.dim() != 3:
+        raise AttnArgumentError(ATTN_ERR_SHAPE)
+    return describe(t.unsqueeze(0))
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale, causal, n_q_heads, n_kv_heads, out, lse,
+                    stream=None):
+    """``attn_fwd_varlen`` with torch tensors: packed sequences, sequence b
+    at rows [cu_seqlens[b], cu_seqlens[b+1]) of q/out (T, Hq, D) and k/v
+    (T, Hkv, D).  cu_seqlens: int32 device tensor [B+1]; max_seqlen: int
+    bound on every length; lse: float32 device tensor [Hq, T] or None."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous() \
+            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor of B+1 offsets")
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 device tensor")
+        if tuple(lse.shape) != (n_q_heads, q.shape[0]):
+            raise ValueError("lse must be [n_q_heads, T]")
+        lse_ptr = ctypes.c_void_p(lse.data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    dq, dk, dv, do = describe_packed(q), describe_packed(k), describe_packed(v), describe_packed(out)
+    code = lib.attn_fwd_varlen(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                               ctypes.c_void_p(cu_seqlens.data_ptr()), int(cu_seqlens.numel() - 1),
+                               int(max_seqlen), ctypes.c_float(0.0 if scale is None else float(scale)),
+                               int(bool(causal)), int(n_q_heads), int(n_kv_heads), ctypes.byref(do), lse_ptr,
+                               ctypes.c_void_p(stream.cuda_stream))
+    check(code)
+    return out, lse
+
+
+def varlen_attention(q, k, v, cu_seqlens, max_seqlen, *, causal=False, scale=None, return_lse=False):
+    """Allocate ``out`` (zero-filled: rows outside every sequence stay 0) and
+    ``lse`` with torch and run ``attn_fwd_varlen``.  Returns out, or
+    (out, lse) with lse float32 [Hq, T]."""
+    import torch
+    out = torch.zeros_like(q)
+    lse = None
+    if return_lse:
+        lse = torch.full((q.shape[1], q.shape[0]), float("-inf"), dtype=torch.float32, device=q.device)
+    attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale, causal, q.shape[1], k.shape[1], out, lse)
     return (out, lse) if return_lse else out
 
 

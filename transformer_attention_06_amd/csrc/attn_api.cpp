@@ -121,6 +121,35 @@ extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const at
     return attn_detail::launch(a);
 }
 
+// Packed variable-length sequences ([ATB-guide] §6.1 and §8.7: one
+// attention operator over whatever lengths arrive; [ops-transformer] §5.2:
+// batch and heads merged into one parallel axis, then the sequence split):
+// the same kernel, each workgroup reading its sequence's offset and length.
+extern "C" int attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                               const int32_t* cu_seqlens, int n_seqs, int64_t max_seqlen, float scale,
+                               int causal, int n_q_heads, int n_kv_heads, const attn_tensor_t* out,
+                               float* lse, void* stream) {
+    attn_detail::LaunchArgs a;
+    bool empty = false;
+    const int rc = prepare(q, k, v, ATTN_MASK_NONE, nullptr, scale, causal, n_q_heads, n_kv_heads, out, lse,
+                           stream, a, empty);
+    if (rc != ATTN_OK) return rc;
+    if (q->B != 1) return ATTN_ERR_SHAPE;  // packed: one (1, T, H, D) buffer per tensor
+    if (n_seqs < 0 || max_seqlen < 0 || max_seqlen > q->S) return ATTN_ERR_SHAPE;
+    if (!cu_seqlens) return ATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return ATTN_ERR_ALIGN;
+    if (empty || n_seqs == 0 || max_seqlen == 0) return ATTN_OK;
+    const int64_t n_qb = (max_seqlen + attn_detail::kBlockM - 1) / attn_detail::kBlockM;
+    if (double(n_seqs) * double(n_q_heads) >= 2147483647.0 ||
+        double(n_qb) * double(n_q_heads) * double(n_seqs) >= 2147483647.0)
+        return ATTN_ERR_UNSUPPORTED;
+    a.total = a.S;
+    a.B = n_seqs;
+    a.S = max_seqlen;
+    a.cu_seqlens = cu_seqlens;
+    return attn_detail::launch(a);
+}
+
 // Rotary embedding of Q and K fused with the attention ([ATB-guide] §4.1,
 // fifth fusion pattern; §8.4 for the rotation and its base of 10000): K is
 // rotated once into k_rot by a bandwidth-bound pass, Q in registers inside
@@ -173,7 +202,7 @@ extern "C" int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_he
     if (B < 0 || Sq < 0 || n_q_heads < 0 || D < 0 || Sk < 0) return -1;
     const int64_t rows = B * int64_t(n_q_heads) * Sq;
     const int64_t n_split = attn_detail::decode_splits(Sk);
-    return n_split * rows * (D + 2) * int64_t(sizeof(float));
+    return n_split * rows * (D + 3) * int64_t(sizeof(float));
 }
 
 extern "C" int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_cache,
@@ -205,6 +234,7 @@ extern "C" int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_ca
     if (B > 65535 || B * n_kv_heads > 65535) return ATTN_ERR_UNSUPPORTED;
     const int64_t rows_per_kv = int64_t(n_q_heads / n_kv_heads) * Sq;
     if ((rows_per_kv + 7) / 8 > 65535) return ATTN_ERR_UNSUPPORTED;
+    if (B * n_q_heads * Sq / 4 + 1 >= int64_t(1) << 31) return ATTN_ERR_UNSUPPORTED;
     const int64_t need = attn_decode_workspace_bytes(B, Sq, n_q_heads, D, Sk);
     if (!q->data || !out->data) return ATTN_ERR_NULL;
     if (Sk > 0 && (!k_cache->data || !v_cache->data)) return ATTN_ERR_NULL;

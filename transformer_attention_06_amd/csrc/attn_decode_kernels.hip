@@ -12,19 +12,28 @@
 // from bytes and FLOPs first), so the design goal is to read every cached
 // byte once, coalesced, from as many workgroups as the chip has:
 //
-//   * one workgroup per (key chunk of 256, batch, kv head, group of 8 query
+//   * one workgroup per (key chunk of 256, batch, kv head, group of query
 //     rows): all query heads sharing the kv head are rows of the same
 //     workgroup, so K and V are read once per chunk;
-//   * 16-byte loads with the head dimension across lanes (LPK lanes per key,
-//     64/LPK keys per wavefront instruction): whole cache rows per load;
-//   * dot products reduced over a key's lanes with DPP and lane swaps, an
-//     online softmax per row in fp32 (lazily rescaled, as in the prefill
-//     kernel), P·V accumulated per lane;
-//   * the chunk's unnormalised (O, max, sum) goes to a caller workspace and a
-//     second kernel merges the chunks by their log-sum-exp (O = Σ_s w_s O_s /
-//     Σ_s w_s l_s with w_s = 2^(m_s - M)), writing O and LSE.
-// This is VALU work on purpose: at one query row per key the contraction is
-// far below the MFMA ridge, and the kernel is bound by HBM.
+//   * 16-bit types: the query rows of a kv head (8 for a Llama-2-70B-style
+//     8:1 GQA step) against the chunk's keys are a real, if short, dense
+//     contraction, so both products run on 32x32x16 MFMA exactly as in the
+//     prefill kernel's transposed form (Sᵀ = K·Qᵀ with one query row per
+//     lane, Oᵀ += Vᵀ·Pᵀ): K and Q operands are 16-byte global loads straight
+//     into registers (K rows taken in the permuted order that makes P an MFMA
+//     operand without data movement), V goes through LDS and is read back
+//     with the transposing LDS read.  Each wavefront owns 64 keys, computes
+//     their scores, softmax and P·V in one pass, and the four wavefronts
+//     combine through LDS.  Up to 32 query rows per workgroup;
+//   * fp32 (a parity path): VALU dot products with the head dimension across
+//     lanes, reduced with DPP and lane swaps, 8 query rows per workgroup;
+//   * the chunk's unnormalised (O, max, sum of the rounded probabilities,
+//     exact sum) goes to a caller workspace and a second kernel, one
+//     wavefront per output row, merges the chunks by their log-sum-exp
+//     (O = Σ_s w_s O_s / Σ_s w_s l_s with w_s = 2^(m_s - M)), writing O and
+//     LSE (from the exact sums).
+// The kernel is bound by reading the cache: the MFMAs take a few per cent of
+// the time the cache bytes take at full HBM bandwidth.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -39,7 +48,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDecThreads = 256;  // 4 wavefronts
 constexpr int kDecChunk = 256;    // keys per workgroup (64 per wavefront)
-constexpr int kDecRows = 8;       // query rows per workgroup
+constexpr int kDecRows = 8;       // query rows per workgroup (fp32 kernel)
+constexpr int kDecRowsMfma = 32;  // query rows per workgroup (MFMA kernel)
 constexpr float kDecRescale = 8.0f;
 
 struct DecParams {
@@ -49,7 +59,8 @@ struct DecParams {
     const int32_t* lens;
     float* ws_o;  // [n_split][B][Hq][Sq][D] unnormalised partial outputs
     float* ws_m;  // [n_split][B][Hq][Sq] partial maxima (log2 units)
-    float* ws_l;  // [n_split][B][Hq][Sq] partial sums
+    float* ws_l;  // [n_split][B][Hq][Sq] partial sums of the rounded probabilities
+    float* ws_e;  // [n_split][B][Hq][Sq] partial sums of the exact probabilities (LSE)
     int B, Sq, Sk, Hq, Hkv, G, R, n_split;
     float sl2;  // scale * log2(e)
     int causal;
@@ -275,45 +286,319 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(DecParams p) 
         if (d == 0) {
             p.ws_m[pi] = M;
             p.ws_l[pi] = lsum;
+            p.ws_e[pi] = lsum;  // fp32 probabilities are not rounded
         }
     }
 }
 
-// Merge of the chunks: one thread per output element.
+// ---- 16-bit types: both products on MFMA -----------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct MfmaOp;
+template <>
+struct MfmaOp<__bf16> {
+    using op_t = bf16x8;
+    static __device__ __forceinline__ f32x16 mma(op_t a, op_t b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct MfmaOp<_Float16> {
+    using op_t = f16x8;
+    static __device__ __forceinline__ f32x16 mma(op_t a, op_t b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// A-operand row permutation: swap bits 2 and 3 of a 0..31 row index.  With K
+// rows (and Vᵀ rows) taken in this order, accumulator register f of a lane
+// in half g holds key (or head dim) 16·((f >> 3) & 1) + 8·g + (f & 7) of its
+// 32-block: eight consecutive positions per register group, which are the
+// eight keys the lane supplies as the P operand of the next product (and
+// eight consecutive head dims of the output).
+__device__ __forceinline__ int perm_row(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
+__device__ __forceinline__ int acc_pos(int f, int g) { return 16 * ((f >> 3) & 1) + 8 * g + (f & 7); }
+
+// Transposing LDS read: in each 16-lane group, lane 4j+q names an 8-byte
+// piece (4 elements of one row); lane 4q+c receives element c of the pieces
+// named by lanes 4j+q, j = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* ptr) {
+    typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(ptr));
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(DecParams p) {
+    using op_t = typename MfmaOp<T>::op_t;
+    constexpr int KW = kDecChunk / 4;  // keys per wavefront (64)
+    constexpr int NC = D / 16;         // MFMA steps along D for Sᵀ
+    constexpr int NDB = D / 32;        // 32-dim blocks of Oᵀ
+    constexpr int ROWP = D + 8;        // LDS row pitch of the V tile (elements): rows shift by 16 bytes
+    constexpr int CPR = D / 8;         // 16-byte chunks per cache row
+    constexpr int NVL = KW * CPR / 64; // V chunks per lane
+    static_assert(4 * NDB * 16 * 64 * 4 <= 4 * KW * ROWP * int(sizeof(T)), "combine stash fits the V tiles");
+    __shared__ __attribute__((aligned(16))) T vt[4 * KW * ROWP];
+    __shared__ float s_ml[4][3][64];
+
+    const int split = blockIdx.x;
+    const int bg = blockIdx.y;  // b * Hkv + g
+    const int rg = blockIdx.z;  // group of 32 query rows
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, gl = lane >> 5;
+    int L = p.lens ? p.lens[b] : p.Sk;
+    L = L < 0 ? 0 : (L > p.Sk ? p.Sk : L);
+    const int k0 = split * kDecChunk + wave * KW;  // this wavefront's first key
+
+    // this lane's query row (the same for both halves of the wavefront)
+    const int rr = rg * kDecRowsMfma + r;
+    const bool live = rr < p.R;
+    const int hq = g * p.G + (live ? rr / p.Sq : 0);
+    const int tok = live ? rr % p.Sq : 0;
+    int jend = 0;  // keys j < jend are visible to this row (end-aligned causal rule)
+    if (live) {
+        jend = p.causal ? L - p.Sq + tok + 1 : L;
+        jend = jend < 0 ? 0 : (jend > L ? L : jend);
+    }
+
+    const int64_t kv_row = int64_t(p.Hkv) * D;  // elements between cache rows
+    const T* kb = static_cast<const T*>(p.k) + (int64_t(b) * p.Sk * p.Hkv + g) * D;
+    const T* vb = static_cast<const T*>(p.v) + (int64_t(b) * p.Sk * p.Hkv + g) * D;
+    T* vw = vt + wave * KW * ROWP;
+
+    // V: the wavefront's 64 cache rows into its LDS tile (zeros past L, so
+    // that a zero probability never meets a stale value)
+    u32x4 vreg[NVL];
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+        const int ch = lane + 64 * i, key = k0 + ch / CPR, c8 = ch % CPR;
+        vreg[i] = key < L ? *reinterpret_cast<const u32x4*>(vb + int64_t(key) * kv_row + 8 * c8) : u32x4{0, 0, 0, 0};
+    }
+    // K operands: block blk, virtual row r is key k0 + 32·blk + perm_row(r);
+    // the lane holds head dims 16c + 8gl .. +7
+    op_t kop[2][NC];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int key = k0 + 32 * blk + perm_row(r);
+        const T* kr = kb + int64_t(key) * kv_row + 8 * gl;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            kop[blk][c] = key < L ? *reinterpret_cast<const op_t*>(kr + 16 * c) : op_t{};
+    }
+    // Q operand: the lane's row, head dims 16c + 8gl .. +7
+    op_t qop[NC];
+    const T* qr = static_cast<const T*>(p.q) + ((int64_t(b) * p.Sq + tok) * p.Hq + hq) * D + 8 * gl;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qop[c] = live ? *reinterpret_cast<const op_t*>(qr + 16 * c) : op_t{};
+
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+        const int ch = lane + 64 * i;
+        *reinterpret_cast<u32x4*>(vw + (ch / CPR) * ROWP + 8 * (ch % CPR)) = vreg[i];
+    }
+
+    // Sᵀ = K·Qᵀ for the 64 keys
+    f32x16 sacc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        sacc[blk] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sacc[blk] = MfmaOp<T>::mma(kop[blk][c], qop[c], sacc[blk]);
+    }
+
+    // softmax over the wavefront's keys (scores in log2 units)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int f = 0; f < 16; ++f) {
+            const int key = k0 + 32 * blk + acc_pos(f, gl);
+            const float sv = key < jend ? sacc[blk][f] * p.sl2 : -INFINITY;
+            sacc[blk][f] = sv;
+            mx = fmaxf(mx, sv);
+        }
+    mx = fmaxf(mx, xor32(mx));
+    const float mu = mx == -INFINITY ? 0.0f : mx;
+    float lsum = 0.0f, lex = 0.0f;
+    op_t pop[2][2];  // P operand of block blk, 16-key step kc: registers 8kc .. 8kc+7
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(sacc[blk][8 * kc + e] - mu);
+                const T pr = static_cast<T>(pe);
+                lex += pe;
+                lsum += float(pr);
+                pop[blk][kc][e] = pr;
+            }
+    lsum += xor32(lsum);
+    lex += xor32(lex);
+
+    // the tile was written by this wavefront's own lanes: wait for the writes
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+
+    // Oᵀ += Vᵀ·Pᵀ: Vᵀ rows (head dims) in the permuted order, read transposed
+    const int tr_key = (r & 15) >> 2;
+    const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                s16x4 half[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int key = 32 * blk + 16 * kc + 8 * gl + 4 * h + tr_key;
+                    half[h] = lds_read_tr16(vw + key * ROWP + 32 * db + tr_col);
+                }
+                const op_t va = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = MfmaOp<T>::mma(va, pop[blk][kc], oacc[db]);
+            }
+
+    // combine the four wavefronts: (m, l, l_exact) and Oᵀ through LDS (the V
+    // tiles are free once every wavefront has passed the barrier)
+    __syncthreads();
+    float* stash = reinterpret_cast<float*>(vt);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int f = 0; f < 16; ++f) stash[((wave * NDB + db) * 16 + f) * 64 + lane] = oacc[db][f];
+    s_ml[wave][0][lane] = mx;
+    s_ml[wave][1][lane] = lsum;
+    s_ml[wave][2][lane] = lex;
+    __syncthreads();
+    if (wave < NDB && live) {
+        const int db = wave;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][lane]);
+        float wt[4], lt = 0.0f, et = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            wt[w] = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s_ml[w][0][lane] - M);
+            lt += wt[w] * s_ml[w][1][lane];
+            et += wt[w] * s_ml[w][2][lane];
+        }
+        const int64_t pi = ((int64_t(split) * p.B + b) * p.Hq + hq) * p.Sq + tok;
+        float* dst = p.ws_o + pi * D + 32 * db + 8 * gl;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float o8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int f = 8 * h + e;
+                float acc = 0.0f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) acc += wt[w] * stash[((w * NDB + db) * 16 + f) * 64 + lane];
+                o8[e] = acc;
+            }
+            // head dims 32db + 16h + 8gl .. +7
+            reinterpret_cast<u32x4*>(dst + 16 * h)[0] = *reinterpret_cast<const u32x4*>(&o8[0]);
+            reinterpret_cast<u32x4*>(dst + 16 * h)[1] = *reinterpret_cast<const u32x4*>(&o8[4]);
+        }
+        if (db == 0 && gl == 0) {
+            p.ws_m[pi] = M;
+            p.ws_l[pi] = lt;
+            p.ws_e[pi] = et;
+        }
+    }
+}
+
+// Merge of the chunks: one wavefront per output row; lanes read the chunk
+// maxima and sums side by side, then accumulate the weighted partial outputs
+// with the head dimension across lanes, eight chunks' loads in flight at once.
 struct MergeParams {
     const float* ws_o;
     const float* ws_m;
     const float* ws_l;
+    const float* ws_e;
     void* out;
     float* lse;
     int64_t rows;  // B * Hq * Sq partial rows, ordered (b, hq, i)
     int B, Sq, Hq, n_split;
 };
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
-    const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (idx >= p.rows * D) return;
-    const int64_t row = idx / D;  // (b * Hq + hq) * Sq + i
-    const int d = int(idx % D);
+    constexpr int DPL = D / 64;  // head dims per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // (b * Hq + hq) * Sq + i
+    if (row >= p.rows) return;                                          // whole wavefront
     float M = -INFINITY;
-    for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.ws_m[s * p.rows + row]);
-    float lsum = 0.0f, osum = 0.0f;
+    for (int s = lane; s < p.n_split; s += 64) M = fmaxf(M, p.ws_m[int64_t(s) * p.rows + row]);
+    M = wave_max(M);
+    float den = 0.0f, dex = 0.0f, acc[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
     if (M != -INFINITY) {
-        for (int s = 0; s < p.n_split; ++s) {
-            const float w = __builtin_amdgcn_exp2f(p.ws_m[s * p.rows + row] - M);
-            lsum += w * p.ws_l[s * p.rows + row];
-            osum += w * p.ws_o[(s * p.rows + row) * D + d];
+        for (int s0 = 0; s0 < p.n_split; s0 += 64) {
+            const int s = s0 + lane;
+            float w = 0.0f;
+            if (s < p.n_split) {
+                const int64_t pi = int64_t(s) * p.rows + row;
+                w = __builtin_amdgcn_exp2f(p.ws_m[pi] - M);
+                den += w * p.ws_l[pi];
+                dex += w * p.ws_e[pi];
+            }
+            const int ns = p.n_split - s0 < 64 ? p.n_split - s0 : 64;
+            int t = 0;
+            for (; t + 8 <= ns; t += 8) {
+                float v[8][DPL];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int i = 0; i < DPL; ++i)
+                        v[u][i] = p.ws_o[(int64_t(s0 + t + u) * p.rows + row) * D + lane + 64 * i];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float wt = __shfl(w, t + u);
+#pragma unroll
+                    for (int i = 0; i < DPL; ++i) acc[i] += wt * v[u][i];
+                }
+            }
+            for (; t < ns; ++t) {
+                const float wt = __shfl(w, t);
+#pragma unroll
+                for (int i = 0; i < DPL; ++i)
+                    acc[i] += wt * p.ws_o[(int64_t(s0 + t) * p.rows + row) * D + lane + 64 * i];
+            }
         }
     }
-    const int i = int(row % p.Sq);
+    den = wave_sum(den);
+    dex = wave_sum(dex);
+    const int i_tok = int(row % p.Sq);
     const int64_t bh = row / p.Sq;
     const int hq = int(bh % p.Hq);
     const int64_t b = bh / p.Hq;
-    T* orow = static_cast<T*>(p.out) + ((b * p.Sq + i) * p.Hq + hq) * D;
-    orow[d] = from_f<T>(lsum > 0.0f ? osum / lsum : 0.0f);
-    if (p.lse && d == 0)
-        p.lse[row] = lsum > 0.0f ? (M + __builtin_amdgcn_logf(lsum)) * 0.69314718055994530942f : -INFINITY;
+    T* orow = static_cast<T*>(p.out) + ((b * p.Sq + i_tok) * p.Hq + hq) * D;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) orow[lane + 64 * i] = from_f<T>(acc[i] * inv);
+    if (p.lse && lane == 0)
+        p.lse[row] = dex > 0.0f ? (M + __builtin_amdgcn_logf(dex)) * 0.69314718055994530942f : -INFINITY;
 }
 
 template <typename T, int D>
@@ -328,6 +613,7 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
     dp.ws_o = ws;
     dp.ws_m = ws + int64_t(a.n_split) * rows * a.D;
     dp.ws_l = dp.ws_m + int64_t(a.n_split) * rows;
+    dp.ws_e = dp.ws_l + int64_t(a.n_split) * rows;
     dp.B = int(a.B);
     dp.Sq = int(a.Sq);
     dp.Sk = int(a.Sk);
@@ -338,15 +624,22 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
     dp.n_split = a.n_split;
     dp.sl2 = a.scale * 1.44269504088896340736f;
     dp.causal = a.causal;
-    const int n_rg = (dp.R + kDecRows - 1) / kDecRows;
-    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(unsigned(a.n_split), unsigned(a.B * a.Hkv), unsigned(n_rg)),
-                       dim3(kDecThreads), 0, static_cast<hipStream_t>(a.stream), dp);
+    if constexpr (sizeof(T) == 2) {
+        const int n_rg = (dp.R + kDecRowsMfma - 1) / kDecRowsMfma;
+        hipLaunchKernelGGL((decode_mfma_kernel<T, D>), dim3(unsigned(a.n_split), unsigned(a.B * a.Hkv), unsigned(n_rg)),
+                           dim3(kDecThreads), 0, static_cast<hipStream_t>(a.stream), dp);
+    } else {
+        const int n_rg = (dp.R + kDecRows - 1) / kDecRows;
+        hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(unsigned(a.n_split), unsigned(a.B * a.Hkv), unsigned(n_rg)),
+                           dim3(kDecThreads), 0, static_cast<hipStream_t>(a.stream), dp);
+    }
     hipError_t e = hipGetLastError();
     if (e == hipSuccess) {
         MergeParams mp;
         mp.ws_o = dp.ws_o;
         mp.ws_m = dp.ws_m;
         mp.ws_l = dp.ws_l;
+        mp.ws_e = dp.ws_e;
         mp.out = a.o;
         mp.lse = a.lse;
         mp.rows = rows;
@@ -354,7 +647,7 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
         mp.Sq = dp.Sq;
         mp.Hq = dp.Hq;
         mp.n_split = dp.n_split;
-        const int64_t blocks = (rows * a.D + 255) / 256;
+        const int64_t blocks = (rows + 3) / 4;
         hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(unsigned(blocks)), dim3(256), 0,
                            static_cast<hipStream_t>(a.stream), mp);
         e = hipGetLastError();

@@ -175,6 +175,8 @@ struct KParams {
     const int32_t* pad_lens;
     int S, Hq, Hkv, group, n_qb, n_units, xcd_chunk;
     int64_t q_bstride, kv_bstride;  // elements per batch
+    const int32_t* cu;              // packed sequences: offsets cu[0..B] into T rows, or null
+    int total;                      // T (packed sequences; S is then the longest length)
     float sl2;                      // scale * log2(e)
     const int32_t* rope_pos;        // (B, S) positions, or null for 0..S-1
     double rope_lb;                 // log2 of the rotary base
@@ -310,6 +312,28 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
         task = wg / p.n_units;
         unit = wg % p.n_units;
     }
+    const int jg = unit % p.group;
+    const int bg = unit / p.group;
+    const int g = bg % p.Hkv;
+    const int b = bg / p.Hkv;
+    const int hq = g * p.group + jg;
+
+    // Rows of this batch entry: with packed sequences (offsets cu[0..B]),
+    // sequence b is rows [cu[b], cu[b+1]) of one (1, T, H, D) buffer, and its
+    // length replaces S.  The offsets are clamped into [0, T] and the length
+    // to the launch's maximum (p.S), so every access stays inside the buffers
+    // whatever the offsets hold.
+    int S = p.S;
+    int64_t row0 = 0;  // first row of this batch entry's sequence
+    if (p.cu) {
+        int s0 = p.cu[b], s1 = p.cu[b + 1];
+        s0 = s0 < 0 ? 0 : (s0 > p.total ? p.total : s0);
+        s1 = s1 < s0 ? s0 : (s1 > p.total ? p.total : s1);
+        S = s1 - s0 < p.S ? s1 - s0 : p.S;
+        row0 = s0;
+    }
+    const int n_qb = p.cu ? (S + BM - 1) / BM : p.n_qb;
+
     // With two groups a task is a pair of query blocks of one (batch, query
     // head): under causal masking the heaviest and the lightest remaining
     // block (qh = n_qb-1-task, ql = task), otherwise two neighbours.  Group 1
@@ -318,27 +342,28 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
     // groups' tile counts, and the heavy block's two partial softmax states
     // are merged through LDS at the end.  With one group a task is one block,
     // heaviest first for the first half of the launch and lightest first for
-    // the second half (two workgroups per CU even out).
+    // the second half (two workgroups per CU even out).  A packed sequence
+    // shorter than the longest has fewer blocks: its surplus tasks leave here,
+    // before any barrier (the whole workgroup shares b and task).
     int qh = task, ql = -1;
     if (NG == 2) {
         if (CAUSAL) {
-            qh = p.n_qb - 1 - task;
+            qh = n_qb - 1 - task;
             ql = task < qh ? task : -1;
+            if (task > qh) return;
         } else {
             qh = 2 * task;
-            ql = 2 * task + 1 < p.n_qb ? 2 * task + 1 : -1;
+            ql = 2 * task + 1 < n_qb ? 2 * task + 1 : -1;
+            if (qh >= n_qb) return;
         }
-    } else if (CAUSAL) {
-        const int half = (p.n_qb + 1) >> 1;
-        qh = task < half ? p.n_qb - 1 - task : task - half;
+    } else {
+        if (task >= n_qb) return;
+        if (CAUSAL) {
+            const int half = (n_qb + 1) >> 1;
+            qh = task < half ? n_qb - 1 - task : task - half;
+        }
     }
-    const int jg = unit % p.group;
-    const int bg = unit / p.group;
-    const int g = bg % p.Hkv;
-    const int b = bg / p.Hkv;
-    const int hq = g * p.group + jg;
 
-    const int S = p.S;
     int key_lim = S;
     if (PAD) {
         const int L = p.pad_lens[b];
@@ -396,9 +421,12 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
 
     const int64_t qstride = int64_t(p.Hq) * D;
     const int64_t kvstride = int64_t(p.Hkv) * D;
-    const T* qbase = static_cast<const T*>(p.q) + int64_t(b) * p.q_bstride + int64_t(hq) * D;
-    const T* kbase = static_cast<const T*>(p.k) + int64_t(b) * p.kv_bstride + int64_t(g) * D;
-    const T* vbase = static_cast<const T*>(p.v) + int64_t(b) * p.kv_bstride + int64_t(g) * D;
+    // element offsets of this batch entry's first row in q / out and in k, v
+    const int64_t q_off = p.cu ? row0 * qstride : int64_t(b) * p.q_bstride;
+    const int64_t kv_off = p.cu ? row0 * kvstride : int64_t(b) * p.kv_bstride;
+    const T* qbase = static_cast<const T*>(p.q) + q_off + int64_t(hq) * D;
+    const T* kbase = static_cast<const T*>(p.k) + kv_off + int64_t(g) * D;
+    const T* vbase = static_cast<const T*>(p.v) + kv_off + int64_t(g) * D;
 
     // ---- tile loads: global -> LDS directly -------------------------------
     // Buffer resources cover this (batch, kv head) slice; rows at or past S
@@ -562,8 +590,7 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
         const float l_e = LSE ? sum_xor32(l_lse) : 0.0f;
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         if (qrow < S) {
-            T* orow = static_cast<T*>(p.o) + int64_t(b) * p.q_bstride + int64_t(qrow) * qstride +
-                      int64_t(hq) * D;
+            T* orow = static_cast<T*>(p.o) + q_off + int64_t(qrow) * qstride + int64_t(hq) * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -582,7 +609,9 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
             if (LSE && gl == 0) {
                 const float lse = l_e > 0.0f ? (m_run + __builtin_amdgcn_logf(l_e)) * 0.69314718055994530942f
                                              : -INFINITY;
-                p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] = lse;
+                // (B, Hq, S); packed sequences: (Hq, T)
+                const int64_t li = p.cu ? int64_t(hq) * p.total + row0 + qrow : (int64_t(b) * p.Hq + hq) * S + qrow;
+                p.lse[li] = lse;
             }
         }
     };
@@ -955,6 +984,8 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     kp.sl2 = a.scale * 1.44269504088896340736f;
     kp.rope_pos = a.rope_pos;
     kp.rope_lb = a.rope_lb;
+    kp.cu = a.cu_seqlens;
+    kp.total = int(a.total);
     constexpr int NG = Groups<T>::value;
     const int n_tasks = NG == 2 ? (kp.n_qb + 1) / 2 : kp.n_qb;
     const int64_t n_wg = int64_t(n_tasks) * kp.n_units;

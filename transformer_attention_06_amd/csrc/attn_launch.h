@@ -28,6 +28,10 @@ struct LaunchArgs {
     const int32_t* rope_pos = nullptr;  // (B, S) positions or null (0..S-1)
     double rope_f[64] = {};             // theta_i / 2pi for i < D/2
     double rope_lb = 0.0;               // log2(base): theta_i = 2^(-2i/D * rope_lb)
+    // packed sequences: B sequences at rows [cu[b], cu[b+1]) of (1, total,
+    // H, D) buffers; S is then the longest length and lse is (Hq, total)
+    const int32_t* cu_seqlens = nullptr;
+    int64_t total = 0;
 };
 
 // Enqueue the kernel; returns ATTN_OK or ATTN_ERR_LAUNCH / ATTN_ERR_DEVICE.

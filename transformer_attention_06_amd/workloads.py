@@ -60,6 +60,11 @@ WORKLOADS = {
         "batched_padded", 2, B=16, S=512, Hq=32, Hkv=32, D=64, dtype="fp16",
         causal=False, mask_kind=MASK_KEY_PADDING, pad_range=(128, 512),
         note="batched short sequences, per-sequence valid key lengths"),
+    "batched_varlen": Workload(
+        "batched_varlen", 2, B=16, S=512, Hq=32, Hkv=32, D=64, dtype="fp16",
+        causal=False, pad_range=(128, 512),
+        note="the batched short sequences packed back to back (no padding): "
+             "16 lengths uniform in [128, 512]"),
     "gqa_llama2_70b": Workload(
         "gqa_llama2_70b", 3, B=2, S=4096, Hq=64, Hkv=8, D=128, dtype="bf16",
         causal=True, outlier_frac=0.01, outlier_mult=20.0,
@@ -101,6 +106,21 @@ def make_inputs(w, seed=None, *, B=None, S=None):
         lo, hi = min(lo, s), min(hi, s)
         pad = rng.integers(lo, hi, size=b, endpoint=True).astype(np.int32)
     return q, k, v, pad
+
+
+def make_varlen_inputs(w, seed=None):
+    """Packed sequences: draw the B lengths (uniform in w.pad_range), then
+    float32 Q (T, Hq, D), K and V (T, Hkv, D) for T = the sum of the lengths.
+    Returns q, k, v and the int64 offsets cu[0..B] (cu[0] = 0)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    lo, hi = w.pad_range
+    lens = rng.integers(lo, hi, size=w.B, endpoint=True)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    t = int(cu[-1])
+    q = rng.standard_normal((t, w.Hq, w.D), dtype=np.float32)
+    k = rng.standard_normal((t, w.Hkv, w.D), dtype=np.float32)
+    v = rng.standard_normal((t, w.Hkv, w.D), dtype=np.float32)
+    return q, k, v, cu
 
 
 def random_inputs(seed, B, S, Hq, Hkv, D, *, dist="normal", df=2.0):
