@@ -29,7 +29,11 @@ cache truncation, the key-split merge by LSE, torch's SDPA), and attention over 
 variable-length sequences (``attention_varlen``) by
 ``tests/oracle_varlen_pins.py`` (the batched oracle at equal lengths, key
 padding standing in for a shorter sequence, torch's SDPA per sequence, the
-uniform-score closed form, independence of sequences).
+uniform-score closed form, independence of sequences), and attention under
+an explicit additive mask tensor (``attention_masked``) by
+``tests/oracle_masked_pins.py`` (the prefill oracle for zero, triangular and
+key-padding masks, torch's SDPA with a float mask under every broadcast
+shape, the per-row shift invariance, fully masked rows).
 """
 
 from .attention import (  # noqa: F401
@@ -55,4 +59,8 @@ from .decode import (  # noqa: F401
 from .varlen import (  # noqa: F401
     check_offsets as varlen_check_offsets,
     attention_varlen,
+)
+from .masked import (  # noqa: F401
+    mask_slice,
+    attention_masked,
 )

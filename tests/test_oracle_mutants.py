@@ -211,3 +211,61 @@ def test_varlen_mutant_is_caught(name):
             except (AssertionError, FloatingPointError, ValueError, IndexError):
                 caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+# --------------------------------------------------------------------------
+# additive mask tensor (oracle/masked.py) against tests/oracle_masked_pins.py
+# --------------------------------------------------------------------------
+import oracle_masked_pins  # noqa: E402
+
+MASKED_SRC = os.path.join(os.path.dirname(oracle.__file__), "masked.py")
+
+MASKED_MUTANTS = {
+    "mask_before_scale": ("scores = (q[b, :, h, :] @ k[b, :, g, :].T) * scale + mask_slice(mask, b, h)",
+                          "scores = (q[b, :, h, :] @ k[b, :, g, :].T + mask_slice(mask, b, h)) * scale"),
+    "mask_subtracted": ("scores = (q[b, :, h, :] @ k[b, :, g, :].T) * scale + mask_slice(mask, b, h)",
+                        "scores = (q[b, :, h, :] @ k[b, :, g, :].T) * scale - mask_slice(mask, b, h)"),
+    "mask_ignored": ("scores = (q[b, :, h, :] @ k[b, :, g, :].T) * scale + mask_slice(mask, b, h)",
+                     "scores = (q[b, :, h, :] @ k[b, :, g, :].T) * scale"),
+    "mask_transposed": ("return mask[b if bm > 1 else 0, h if hm > 1 else 0]",
+                        "return mask[b if bm > 1 else 0, h if hm > 1 else 0].T"),
+    "mask_batch_broadcast_wrong": ("return mask[b if bm > 1 else 0, h if hm > 1 else 0]",
+                                   "return mask[0, h if hm > 1 else 0]"),
+    "mask_head_from_kv": ("return mask[b if bm > 1 else 0, h if hm > 1 else 0]",
+                          "return mask[b if bm > 1 else 0, (h // 2) if hm > 1 else 0]"),
+    "causal_ignored": ("            if causal:\n                scores = np.where(above, -np.inf, scores)",
+                       "            if False:\n                scores = np.where(above, -np.inf, scores)"),
+    "causal_strict": ("above = np.triu(np.ones((s, s), dtype=bool), k=1)",
+                      "above = np.triu(np.ones((s, s), dtype=bool), k=0)"),
+    "unguarded_max": ("e = np.exp(scores - m_safe[:, None])", "e = np.exp(scores - m[:, None])"),
+    "lse_missing_max": ("lse[b, h, :] = np.where(has_key, m_safe + np.log(safe), -np.inf)",
+                        "lse[b, h, :] = np.where(has_key, np.log(safe), -np.inf)"),
+    "gqa_interleaved": ("g = (h * hkv) // hq", "g = h % hkv"),
+    "default_scale_1_over_d": ("scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d"),
+}
+
+
+def _load_masked_mutant(find, repl):
+    src = open(MASKED_SRC).read()
+    assert src.count(find) == 1, f"mutation anchor not unique/found: {find!r}"
+    mod = types.ModuleType("oracle_masked_mutant")
+    exec(compile(src.replace(find, repl), "oracle_masked_mutant.py", "exec"), mod.__dict__)
+    # the pins also use the (pinned) prefill oracle through the same module
+    mod.attention = oracle.attention
+    mod.MASK_KEY_PADDING = oracle.MASK_KEY_PADDING
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MASKED_MUTANTS))
+def test_masked_mutant_is_caught(name):
+    mod = _load_masked_mutant(*MASKED_MUTANTS[name])
+    caught = []
+    import warnings
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        for pin in oracle_masked_pins.ALL_PINS:
+            try:
+                pin(mod)
+            except (AssertionError, FloatingPointError, ValueError, IndexError):
+                caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"

@@ -29,3 +29,11 @@ import oracle_varlen_pins  # noqa: E402
 @pytest.mark.parametrize("pin", oracle_varlen_pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_varlen_pin(pin):
     pin(oracle)
+
+
+import oracle_masked_pins  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", oracle_masked_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_masked_pin(pin):
+    pin(oracle)
