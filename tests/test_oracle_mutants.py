@@ -237,7 +237,7 @@ MASKED_MUTANTS = {
                        "            if False:\n                scores = np.where(above, -np.inf, scores)"),
     "causal_strict": ("above = np.triu(np.ones((s, s), dtype=bool), k=1)",
                       "above = np.triu(np.ones((s, s), dtype=bool), k=0)"),
-    "unguarded_max": ("e = np.exp(scores - m_safe[:, None])", "e = np.exp(scores - m[:, None])"),
+    "masked_rows_unguarded": ("has_key = np.isfinite(m)", "has_key = np.ones_like(m, dtype=bool)"),
     "lse_missing_max": ("lse[b, h, :] = np.where(has_key, m_safe + np.log(safe), -np.inf)",
                         "lse[b, h, :] = np.where(has_key, np.log(safe), -np.inf)"),
     "gqa_interleaved": ("g = (h * hkv) // hq", "g = h % hkv"),
