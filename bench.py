@@ -15,7 +15,7 @@ kernel source, else null.  The cpu_baseline block times the fp64 CPU oracle on
 a bounded sample of heads of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--all] [--sweep] [--rope] [--decode] [--varlen]
+                    [--no-cpu-baseline] [--all] [--sweep] [--rope] [--decode] [--varlen] [--masked]
                     [--copy-calibration]
 """
 
@@ -296,6 +296,54 @@ def bench_varlen(steps, warmup, use_graph=True, warmup_s=0.0, name="batched_varl
                        "note": "same sequences through attn_fwd key padding at S = 512"}}
 
 
+def bench_masked(steps, warmup, use_graph=True, warmup_s=0.0, name=DEFAULT_WORKLOAD):
+    """attn_fwd_masked on the Llama-2-7B-shaped causal prefill: a (1, 1, S, S)
+    additive mask (N(0,1)·0.5 shifts, -inf above the diagonal) with the causal
+    flag on, so the metric's FLOP count (halved for causal) applies; plain
+    attn_fwd on the same Q, K, V is timed alongside."""
+    import torch
+    from transformer_attention_06_amd import attn as A
+    from transformer_attention_06_amd import workloads as W
+    w = W.WORKLOADS[name]
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[w.dtype]
+    q, k, v, _ = W.make_inputs(w)
+    qd, kd, vd = (torch.from_numpy(x).to(dt).cuda() for x in (q, k, v))
+    rng = np.random.default_rng(w.seed + 100)
+    m = (rng.standard_normal((1, 1, w.S, w.S)) * 0.5).astype(np.float32)
+    m[0, 0][np.triu(np.ones((w.S, w.S), bool), 1)] = -np.inf
+    md = torch.from_numpy(m).to(dt).cuda()
+    out = torch.empty_like(qd)
+
+    def step():
+        A.attn_fwd_masked(qd, kd, vd, md, None, True, w.Hq, w.Hkv, out, None)
+
+    ms_wall, ms_dev, done = time_steps(step, steps, warmup, use_graph, warmup_s)
+
+    def step_plain():
+        A.attn_fwd(qd, kd, vd, A.ATTN_MASK_NONE, None, None, True, w.Hq, w.Hkv, out, None)
+
+    _, ms_plain, _ = time_steps(step_plain, steps, warmup, use_graph, warmup_s)
+    fl = metric_flops(w)
+    peak = PEAK_TFLOPS[w.dtype]
+    el = 2
+    # Q, K, V, O once, plus the mask blocks on or below the diagonal
+    nbytes = min_hbm_bytes(w, None) + (w.S * (w.S + 1) // 2) * el
+    achieved = fl / (ms_dev * 1e-3) / 1e12
+    return {"metric": "fused attention fwd with an additive mask tensor: TFLOP/s", "value": round(fl / (ms_wall * 1e-3) / 1e12, 3),
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": done, "ms_per_step": round(ms_wall, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+            "data": "synthetic (seeded N(0,1) Q, K, V; N(0,1)*0.5 mask with -inf above the diagonal)",
+            "config": {"workload": name + "_masked", "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                       "causal": True, "mask_shape": [1, 1, w.S, w.S],
+                       "timing": "hip_graph_replay" if use_graph else "eager_launches"},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                         "frac": round(achieved / peak, 4), "traffic": None,
+                         "kernel_us_mean": round(ms_dev * 1e3, 3), "flops_per_launch": fl,
+                         "min_hbm_bytes_per_launch": nbytes},
+            "attn_fwd_same_inputs": {"kernel_us_mean": round(ms_plain * 1e3, 3),
+                                     "tflops": round(fl / (ms_plain * 1e-3) / 1e12, 3)}}
+
+
 def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0, rope=False):
     from transformer_attention_06_amd import workloads as W
     w = W.WORKLOADS[name]
@@ -367,6 +415,8 @@ def main():
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
     ap.add_argument("--decode", action="store_true",
                     help="decode attention over a KV cache (attn_fwd_decode), Llama-2-70B shapes, HBM roofline")
+    ap.add_argument("--masked", action="store_true",
+                    help="additive mask tensor (attn_fwd_masked) on the Llama-2-7B-shaped prefill")
     ap.add_argument("--varlen", action="store_true",
                     help="packed variable-length sequences (attn_fwd_varlen) vs the same lengths padded")
     ap.add_argument("--rope", action="store_true",
@@ -392,6 +442,9 @@ def main():
     if args.decode:
         for name in DECODE_SHAPES:
             print(json.dumps(bench_decode(name, args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)
+        return
+    if args.masked:
+        print(json.dumps(bench_masked(args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)
         return
     if args.varlen:
         print(json.dumps(bench_varlen(args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)

@@ -159,6 +159,37 @@ int attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k, const attn_t
                     int n_q_heads, int n_kv_heads, const attn_tensor_t* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_masked — attn_fwd with an explicit additive mask tensor.
+ *
+ * The page "CANN-ATB图优化-昇腾NPU怎么把PyTorch计算图改造成融合算子" (Pattern 2)
+ * fuses Q·Kᵀ → Scale → Mask → Softmax → ·V into FlashAttention(Q, K, V, mask,
+ * scale), the mask entering after the scale; the ATB engineering guide
+ * (hwcomputing.csdn.net/6a59a88310ee7a33f28e5ce9) §8.2 passes the mask to the
+ * attention operator as one more FP16 input tensor.  Computed as attn_fwd
+ * documents, with the scores
+ *
+ *   S_ij = (Q_i · K_j) · scale + M[b', h', i, j]
+ *
+ * where M is (mask_B, mask_H, S, S), contiguous, row-major, in q's dtype,
+ * broadcast over batch (mask_B == 1: b' = 0; mask_B == B: b' = b) and query
+ * heads (mask_H == 1 or Hq).  -inf hides a key; a row whose every score is
+ * -inf is written as zeros with LSE -inf.  causal (0/1) composes with the
+ * mask (j > i is hidden as well).
+ *
+ *   mask        device pointer, 16-byte aligned (ATTN_ERR_ALIGN), values
+ *               finite or -inf.
+ *   mask_B      1 or q->B; mask_H  1 or n_q_heads (else ATTN_ERR_MASK).
+ *   q, k, v, scale, causal, n_q_heads, n_kv_heads, out, lse, stream: as for
+ *               attn_fwd (no key-padding argument: a mask expresses it).
+ *
+ * Supported: bf16 and fp16 (fp32 returns ATTN_ERR_UNSUPPORTED), D in {64,
+ * 128}, B <= 65535.  One launch; all checks precede it.
+ */
+int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                    const void* mask, int64_t mask_B, int64_t mask_H, float scale, int causal,
+                    int n_q_heads, int n_kv_heads, const attn_tensor_t* out, float* lse, void* stream);
+
+/*
  * attn_fwd_rope — rotary position embedding of Q and K fused with attn_fwd.
  *
  * The fifth fusion pattern of the ATB engineering guide

@@ -270,3 +270,32 @@ def test_varlen_empty_returns_ok_without_launch(lib):
     assert call_var(lib, q, k, v, o, max_len=0) == A.ATTN_OK
     z = dict(S=0, data=0)
     assert call_var(lib, T(H=4, **z), T(H=2, **z), T(H=2, **z), T(H=4, **z), max_len=0) == A.ATTN_OK
+
+
+# --------------------------------------------------------------------------
+# attn_fwd_masked: additive mask tensor, host only
+# --------------------------------------------------------------------------
+def call_mask(lib, q, k, v, out, mask=FAKE + 0x300000, mb=1, mh=1, causal=0, lse=None):
+    return lib.attn_fwd_masked(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), mask, ctypes.c_int64(mb),
+                               ctypes.c_int64(mh), ctypes.c_float(0.0), causal, q.H, k.H, ctypes.byref(out), lse,
+                               None)
+
+
+def test_masked_checks(lib):
+    q, k, v, o = T(B=2, H=4), T(B=2, H=2), T(B=2, H=2), T(B=2, H=4)
+    f32 = dict(dtype=A.ATTN_F32)
+    assert call_mask(lib, T(B=2, H=4, **f32), T(B=2, H=2, **f32), T(B=2, H=2, **f32),
+                     T(B=2, H=4, **f32)) == A.ATTN_ERR_UNSUPPORTED            # 16-bit types only
+    assert call_mask(lib, q, k, v, o, mb=3) == A.ATTN_ERR_MASK                # batch dim neither 1 nor B
+    assert call_mask(lib, q, k, v, o, mh=2) == A.ATTN_ERR_MASK                # head dim neither 1 nor Hq
+    assert call_mask(lib, q, k, v, o, mask=None) == A.ATTN_ERR_NULL
+    assert call_mask(lib, q, k, v, o, mask=FAKE + 8) == A.ATTN_ERR_ALIGN
+    assert call_mask(lib, q, k, v, o, causal=2) == A.ATTN_ERR_MASK
+    assert call_mask(lib, q, T(B=2, H=3), T(B=2, H=3), o) == A.ATTN_ERR_HEADS
+    assert call_mask(lib, T(B=2, H=4, D=96), T(B=2, H=2, D=96), T(B=2, H=2, D=96),
+                     T(B=2, H=4, D=96)) == A.ATTN_ERR_UNSUPPORTED
+
+
+def test_masked_empty_returns_ok_without_launch(lib):
+    z = dict(S=0)
+    assert call_mask(lib, T(H=4, **z), T(H=2, **z), T(H=2, **z), T(H=4, **z), mask=None) == A.ATTN_OK

@@ -1,0 +1,141 @@
+"""attn_fwd_masked (explicit additive mask tensor) vs the fp64 masked oracle,
+through the C ABI.
+
+Cases cover every broadcast shape of the mask ((1|B, 1|Hq, S, S)), sequence
+lengths at and around the 64-key tile and 128-row block (including S not a
+multiple of 8, where mask rows are not 16-byte aligned), finite shifts and
+-inf holes, fully masked rows, the causal flag composed with a mask, GQA,
+bf16 and fp16, D = 64 and 128, and a Llama-2-7B-shaped layer (S = 2048,
+D = 128, bf16) with a causal mask given as a tensor.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import prep, to_np
+from tolerances import assert_parity
+from transformer_attention_06_amd import attn as A
+
+pytestmark = pytest.mark.gpu
+
+
+def _mask(rng, shape, hole=0.3, amp=2.0):
+    m = (rng.standard_normal(shape) * amp).astype(np.float32)
+    m[rng.random(shape) < hole] = -np.inf
+    return m
+
+
+def _run(seed, B, S, Hq, Hkv, D, dtype, mshape, causal, *, hole=0.3, full_rows=(), lse=True, scale=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    m = _mask(rng, mshape, hole)
+    for r in full_rows:
+        m[..., r, :] = -np.inf
+    qd, qn = prep(q, dtype)
+    kd, kn = prep(k, dtype)
+    vd, vn = prep(v, dtype)
+    md, mn = prep(m, dtype)
+    print(f"masked case seed={seed} B{B} S{S} H{Hq}/{Hkv} D{D} {dtype} mask={mshape} causal={causal}", flush=True)
+    out, l = A.masked_attention(qd, kd, vd, md, causal=causal, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_masked(qn, kn, vn, mn, causal=causal, scale=scale)
+    return to_np(out), l.cpu().numpy(), ro, rl
+
+
+SHAPES = lambda B, Hq, S: [(1, 1, S, S), (B, 1, S, S), (1, Hq, S, S), (B, Hq, S, S)]
+
+CASES = [
+    # seed, B, S, Hq, Hkv, D, dtype, causal
+    (1, 2, 200, 4, 2, 128, "bf16", False),
+    (2, 2, 200, 4, 2, 128, "bf16", True),
+    (3, 2, 203, 4, 4, 64, "fp16", False),   # S % 8 != 0: element-wise mask loads
+    (4, 1, 129, 2, 1, 64, "bf16", True),
+    (5, 3, 65, 3, 1, 128, "fp16", True),
+    (6, 1, 1, 2, 2, 64, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[6]}-D{c[5]}-S{c[2]}-c{int(c[7])}")
+@pytest.mark.parametrize("si", range(4), ids=["m11", "mB1", "m1H", "mBH"])
+def test_masked(case, si):
+    seed, B, S, Hq, Hkv, D, dtype, causal = case
+    shape = SHAPES(B, Hq, S)[si]
+    o, l, ro, rl = _run(seed * 10 + si, B, S, Hq, Hkv, D, dtype, shape, causal)
+    assert_parity(o, ro, dtype, lse=l, lse_ref=rl, what=f"masked {case} {shape}")
+
+
+def test_masked_fully_masked_rows():
+    """Rows whose every key is -inf: zeros and LSE -inf; neighbours exact."""
+    o, l, ro, rl = _run(11, 2, 150, 2, 1, 128, "bf16", (1, 1, 150, 150), False, full_rows=(0, 64, 127, 149))
+    assert np.all(o[:, [0, 64, 127, 149]] == 0.0)
+    assert np.all(np.isneginf(l[:, :, [0, 64, 127, 149]]))
+    assert_parity(o, ro, "bf16", lse=l, lse_ref=rl, what="fully masked rows")
+
+
+def test_masked_all_finite_shifts_and_scale():
+    """No holes, large finite shifts (|M| up to ~20), a given scale."""
+    o, l, ro, rl = _run(12, 1, 256, 4, 2, 64, "fp16", (1, 4, 256, 256), True, hole=0.0, scale=0.09)
+    assert_parity(o, ro, "fp16", lse=l, lse_ref=rl, what="finite shifts")
+
+
+def test_masked_triangle_equals_causal_flag_and_padding():
+    """A -inf upper triangle as the mask (flag off) and a key-padding mask
+    match the oracle, as the flag / key padding would."""
+    rng = np.random.default_rng(13)
+    B, S, Hq, Hkv, D = 2, 300, 4, 2, 128
+    q, k, v = (rng.standard_normal((B, S, h, D)).astype(np.float32) for h in (Hq, Hkv, Hkv))
+    qd, qn = prep(q, "bf16")
+    kd, kn = prep(k, "bf16")
+    vd, vn = prep(v, "bf16")
+    tri = np.where(np.triu(np.ones((S, S), bool), 1), -np.inf, 0.0).astype(np.float32)[None, None]
+    md, _ = prep(tri, "bf16")
+    print("masked case triangle", flush=True)
+    out, l = A.masked_attention(qd, kd, vd, md, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(qn, kn, vn, causal=True)
+    assert_parity(to_np(out), ro, "bf16", lse=l.cpu().numpy(), lse_ref=rl, what="triangle mask")
+    lens = np.array([300, 77], np.int32)
+    pad = np.zeros((B, 1, S, S), np.float32)
+    for b, L in enumerate(lens):
+        pad[b, :, :, L:] = -np.inf
+    pd, _ = prep(pad, "bf16")
+    print("masked case key padding", flush=True)
+    out, l = A.masked_attention(qd, kd, vd, pd, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(qn, kn, vn, causal=True, mask_kind=oracle.MASK_KEY_PADDING, pad_lens=lens)
+    assert_parity(to_np(out), ro, "bf16", lse=l.cpu().numpy(), lse_ref=rl, what="padding mask")
+
+
+def test_masked_rejects_fp32_and_bad_shapes():
+    q = torch.zeros((1, 64, 2, 64), dtype=torch.float32, device="cuda")
+    m = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        A.masked_attention(q, q, q, m)
+    qb = q.to(torch.bfloat16)
+    with pytest.raises(ValueError):
+        A.masked_attention(qb, qb, qb, torch.zeros((1, 3, 64, 64), dtype=torch.bfloat16, device="cuda"))
+
+
+@pytest.mark.slow
+def test_masked_llama2_7b_layer():
+    """Llama-2-7B-shaped rows (S = 2048, D = 128, bf16), 8 of its 32 heads,
+    with the causal mask given as a (1, 1, S, S) tensor plus random finite
+    shifts, against the oracle."""
+    rng = np.random.default_rng(14)
+    B, S, H, D = 1, 2048, 8, 128
+    q, k, v = (rng.standard_normal((B, S, H, D)).astype(np.float32) for _ in range(3))
+    m = (rng.standard_normal((1, 1, S, S)) * 0.5).astype(np.float32)
+    m[0, 0][np.triu(np.ones((S, S), bool), 1)] = -np.inf
+    qd, qn = prep(q, "bf16")
+    kd, kn = prep(k, "bf16")
+    vd, vn = prep(v, "bf16")
+    md, mn = prep(m, "bf16")
+    print("masked case llama2-7b-shaped", flush=True)
+    out, l = A.masked_attention(qd, kd, vd, md, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_masked(qn, kn, vn, mn)
+    assert_parity(to_np(out), ro, "bf16", lse=l.cpu().numpy(), lse_ref=rl, what="llama2-7b masked")

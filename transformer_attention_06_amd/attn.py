@@ -28,7 +28,7 @@ ATTN_ERR_DEVICE = -9
 ATTN_ERR_ALIAS = -10
 ATTN_ERR_WORKSPACE = -11
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_rope", "attn_fwd_decode",
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_masked", "attn_fwd_rope", "attn_fwd_decode",
                     "attn_decode_workspace_bytes", "attn_strerror", "attn_version")
 
 
@@ -65,6 +65,9 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd_varlen.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_fwd_varlen.restype = ctypes.c_int
+    lib.attn_fwd_masked.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd_masked.restype = ctypes.c_int
     lib.attn_fwd_rope.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, P, P,
                                   ctypes.c_void_p, ctypes.c_void_p]
@@ -269,6 +272,43 @@ def varlen_attention(q, k, v, cu_seqlens, max_seqlen, *, causal=False, scale=Non
     if return_lse:
         lse = torch.full((q.shape[1], q.shape[0]), float("-inf"), dtype=torch.float32, device=q.device)
     attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen, scale, causal, q.shape[1], k.shape[1], out, lse)
+    return (out, lse) if return_lse else out
+
+
+def attn_fwd_masked(q, k, v, mask, scale, causal, n_q_heads, n_kv_heads, out, lse, stream=None):
+    """``attn_fwd_masked`` with torch tensors: q, k, v, out as for attn_fwd
+    (bf16/fp16); mask: contiguous (1 or B, 1 or Hq, S, S) device tensor of
+    q's dtype, added to the scaled scores (-inf hides a key)."""
+    import torch
+    lib = load_library()
+    _, lse_ptr = _common_ptrs(q, k, v, out, None, lse, n_q_heads)
+    if not mask.is_cuda or not mask.is_contiguous() or mask.dim() != 4:
+        raise ValueError("mask must be a contiguous 4-D device tensor (1|B, 1|Hq, S, S)")
+    if mask.dtype != q.dtype:
+        raise AttnArgumentError(ATTN_ERR_DTYPE)
+    if tuple(mask.shape[2:]) != (q.shape[1], q.shape[1]):
+        raise AttnArgumentError(ATTN_ERR_MASK)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
+    code = lib.attn_fwd_masked(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.c_void_p(mask.data_ptr()),
+                               int(mask.shape[0]), int(mask.shape[1]),
+                               ctypes.c_float(0.0 if scale is None else float(scale)), int(bool(causal)),
+                               int(n_q_heads), int(n_kv_heads), ctypes.byref(do), lse_ptr,
+                               ctypes.c_void_p(stream.cuda_stream))
+    check(code)
+    return out, lse
+
+
+def masked_attention(q, k, v, mask, *, causal=False, scale=None, return_lse=False):
+    """Allocate ``out`` (and ``lse``) with torch and run ``attn_fwd_masked``.
+    Returns out, or (out, lse) with lse float32 [B, Hq, S]."""
+    import torch
+    out = torch.empty_like(q)
+    lse = None
+    if return_lse:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    attn_fwd_masked(q, k, v, mask, scale, causal, q.shape[2], k.shape[2], out, lse)
     return (out, lse) if return_lse else out
 
 

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_fwd.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", "attn_decode_kernels.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", "attn_decode_kernels.hip", "attn_masked_kernels.hip"]
 
 # Packed-fp32 VALU forms are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -150,6 +150,31 @@ extern "C" int attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k, c
     return attn_detail::launch(a);
 }
 
+// Explicit additive mask tensor ([graph-opt] Pattern 2's FlashAttention(Q, K,
+// V, mask, scale); [ATB-guide] §8.2 passes the mask as one more FP16 input):
+// a kernel of its own that reads the mask block of every tile.
+extern "C" int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                               const void* mask, int64_t mask_B, int64_t mask_H, float scale, int causal,
+                               int n_q_heads, int n_kv_heads, const attn_tensor_t* out, float* lse,
+                               void* stream) {
+    attn_detail::LaunchArgs a;
+    bool empty = false;
+    const int rc = prepare(q, k, v, ATTN_MASK_NONE, nullptr, scale, causal, n_q_heads, n_kv_heads, out, lse,
+                           stream, a, empty);
+    if (rc != ATTN_OK) return rc;
+    if (q->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;  // 16-bit types only
+    if (mask_B != 1 && mask_B != q->B) return ATTN_ERR_MASK;
+    if (mask_H != 1 && mask_H != n_q_heads) return ATTN_ERR_MASK;
+    if (empty) return ATTN_OK;
+    if (!mask) return ATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(mask) & 15u) != 0) return ATTN_ERR_ALIGN;
+    if (q->B > 65535) return ATTN_ERR_UNSUPPORTED;  // grid z
+    a.mask = mask;
+    a.mask_b = mask_B != 1 ? 1 : 0;
+    a.mask_h = mask_H != 1 ? 1 : 0;
+    return attn_detail::launch_masked(a);
+}
+
 // Rotary embedding of Q and K fused with the attention ([ATB-guide] §4.1,
 // fifth fusion pattern; §8.4 for the rotation and its base of 10000): K is
 // rotated once into k_rot by a bandwidth-bound pass, Q in registers inside

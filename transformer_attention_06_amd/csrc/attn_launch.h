@@ -32,10 +32,17 @@ struct LaunchArgs {
     // H, D) buffers; S is then the longest length and lse is (Hq, total)
     const int32_t* cu_seqlens = nullptr;
     int64_t total = 0;
+    // additive mask (Bm, Hm, S, S) in the input type; mask_b / mask_h are 1
+    // when the mask has a batch dimension of B / a head dimension of Hq
+    const void* mask = nullptr;
+    int mask_b = 0, mask_h = 0;
 };
 
 // Enqueue the kernel; returns ATTN_OK or ATTN_ERR_LAUNCH / ATTN_ERR_DEVICE.
 int launch(const LaunchArgs& a);
+
+// Enqueue the attention with an additive mask tensor (16-bit types only).
+int launch_masked(const LaunchArgs& a);
 
 // Enqueue the rotary embedding of K (a.k, layout (B, S, Hkv, D)) into
 // k_out (same layout; may be a.k itself) with a.rope_pos and a.rope_f.

@@ -1,0 +1,310 @@
+// attn_masked_kernels.hip — fused attention forward with an explicit additive
+// mask tensor (gfx950).
+//
+// "CANN-ATB图优化-昇腾NPU怎么把PyTorch计算图改造成融合算子" Pattern 2 fuses
+// Q·Kᵀ → Scale → Mask → Softmax → ·V into FlashAttention(Q, K, V, mask,
+// scale), and the ATB engineering guide (hwcomputing.csdn.net/
+// 6a59a88310ee7a33f28e5ce9) §8.2 hands the mask to the operator as one more
+// FP16 input tensor.  Here the mask M (1 or B, 1 or Hq, S, S), in the input
+// type, is added to the scaled scores; -inf hides a key.
+//
+// One workgroup (4 wavefronts) owns one (batch, query head, 128-row query
+// block); each wavefront owns 32 query rows, one per lane, in the transposed
+// MFMA form of the prefill kernel: Sᵀ = K·Qᵀ and Oᵀ += Vᵀ·Pᵀ on 32x32x16
+// MFMA.  Per 64-key tile every lane loads the 32 mask values of its row that
+// its score registers hold (four 16-byte loads: the permuted K order makes
+// them four runs of 8 consecutive keys), K operands come straight from global
+// memory, and the V tile is staged once per workgroup in LDS and read back
+// with the transposing LDS read.  The online softmax keeps fp32 running max
+// and sums per row ("ops-transformer：Transformer算子融合与推理加速实战" §3.2)
+// and rescales the output accumulator whenever the max rises.  Unlike the
+// unmasked kernel this loop is not software-pipelined: every tile reads its
+// own mask block, and the tile loop waits for its loads.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn_fwd.h"
+#include "attn_launch.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Op;
+template <>
+struct Op<__bf16> {
+    using op_t = bf16x8;
+    static __device__ __forceinline__ f32x16 mma(op_t a, op_t b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Op<_Float16> {
+    using op_t = f16x8;
+    static __device__ __forceinline__ f32x16 mma(op_t a, op_t b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+constexpr int kMThreads = 256;  // 4 wavefronts
+constexpr int kMRows = 128;     // query rows per workgroup
+constexpr int kMKeys = 64;      // keys per tile
+
+struct MParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* mask;  // (Bm, Hm, S, S) in the input type
+    void* o;
+    float* lse;
+    int S, Hq, Hkv, group;
+    int mask_b, mask_h;  // 1 when the mask has a batch (head) dimension of B (Hq)
+    float sl2;           // scale * log2(e)
+};
+
+// A-operand row permutation (swap bits 2 and 3 of a 0..31 row index) and the
+// key / head dim that accumulator register f of a lane in half g then holds
+// within its 32-block: 16·((f >> 3) & 1) + 8·g + (f & 7).
+__device__ __forceinline__ int perm_row(int r) { return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1); }
+__device__ __forceinline__ int acc_pos(int f, int g) { return 16 * ((f >> 3) & 1) + 8 * g + (f & 7); }
+
+// Transposing LDS read: in each 16-lane group, lane 4j+q names an 8-byte
+// piece (4 elements of one row); lane 4q+c receives element c of the pieces
+// named by lanes 4j+q, j = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* ptr) {
+    typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(ptr));
+}
+
+// value held by lane l ^ 32
+__device__ __forceinline__ float xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+template <typename T, int D, bool CAUSAL, bool LSE>
+__global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
+    using op_t = typename Op<T>::op_t;
+    constexpr int NC = D / 16;                     // MFMA steps along D for Sᵀ
+    constexpr int NDB = D / 32;                    // 32-dim blocks of Oᵀ
+    constexpr int ROWP = D + 8;                    // LDS row pitch of the V tile (elements)
+    constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    constexpr int NVL = kMKeys * CPR / kMThreads;  // V chunks per thread
+    static_assert(NVL * kMThreads == kMKeys * CPR, "V tile split over the workgroup");
+    __shared__ __attribute__((aligned(16))) T vt[kMKeys * ROWP];
+
+    // causal: heavy query blocks are dispatched first
+    const int qb = CAUSAL ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
+    const int hq = blockIdx.y, b = blockIdx.z;
+    const int g = hq / p.group;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, gl = lane >> 5;
+    const int S = p.S;
+    const int q0 = qb * kMRows;
+    const int qrow = q0 + wave * 32 + r;
+    const bool live = qrow < S;
+
+    const int64_t qstride = int64_t(p.Hq) * D;
+    const int64_t kvstride = int64_t(p.Hkv) * D;
+    const T* kb = static_cast<const T*>(p.k) + int64_t(b) * S * kvstride + int64_t(g) * D;
+    const T* vb = static_cast<const T*>(p.v) + int64_t(b) * S * kvstride + int64_t(g) * D;
+    const int64_t plane = int64_t(p.mask_b ? b : 0) * (p.mask_h ? p.Hq : 1) + (p.mask_h ? hq : 0);
+    const T* mrow = static_cast<const T*>(p.mask) + (plane * S + (live ? qrow : 0)) * int64_t(S);
+    const bool vec_mask = (S & 7) == 0;  // mask rows 16-byte aligned
+
+    // Q operand: the lane's row, head dims 16c + 8gl .. +7
+    op_t qop[NC];
+    const T* qr = static_cast<const T*>(p.q) + (int64_t(b) * S + qrow) * qstride + int64_t(hq) * D + 8 * gl;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qop[c] = live ? *reinterpret_cast<const op_t*>(qr + 16 * c) : op_t{};
+
+    const int kend = CAUSAL ? (S < q0 + kMRows ? S : q0 + kMRows) : S;
+    const int ntile = (kend + kMKeys - 1) / kMKeys;
+    const int tr_key = (r & 15) >> 2;
+    const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
+    float m_run = -INFINITY, l_run = 0.0f, l_ex = 0.0f;
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+
+    for (int t = 0; t < ntile; ++t) {
+        const int k0 = t * kMKeys;
+        // V tile rows (zeros past S), K operands (virtual row r of block blk
+        // is key k0 + 32·blk + perm_row(r)), the lane's mask values
+        u32x4 vreg[NVL];
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int ch = tid + kMThreads * i, key = k0 + ch / CPR;
+            vreg[i] = key < S ? *reinterpret_cast<const u32x4*>(vb + int64_t(key) * kvstride + 8 * (ch % CPR))
+                              : u32x4{0, 0, 0, 0};
+        }
+        op_t kop[2][NC];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int key = k0 + 32 * blk + perm_row(r);
+            const T* kr = kb + int64_t(key) * kvstride + 8 * gl;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) kop[blk][c] = key < S ? *reinterpret_cast<const op_t*>(kr + 16 * c) : op_t{};
+        }
+        // mask values of keys k0 + 32·blk + 16·h + 8·gl + e (e < 8): the keys
+        // of score registers 8h + e of block blk
+        op_t mraw[2][2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int key0 = k0 + 32 * blk + 16 * h + 8 * gl;
+                if (live && vec_mask && key0 + 8 <= S) {
+                    mraw[blk][h] = *reinterpret_cast<const op_t*>(mrow + key0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mraw[blk][h][e] = (live && key0 + e < S) ? mrow[key0 + e] : T(0.0f);
+                }
+            }
+        __syncthreads();  // every wavefront is done reading the previous V tile
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) {
+            const int ch = tid + kMThreads * i;
+            *reinterpret_cast<u32x4*>(vt + (ch / CPR) * ROWP + 8 * (ch % CPR)) = vreg[i];
+        }
+        __syncthreads();  // the V tile is in place
+
+        // Sᵀ = K·Qᵀ
+        f32x16 sacc[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            sacc[blk] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) sacc[blk] = Op<T>::mma(kop[blk][c], qop[c], sacc[blk]);
+        }
+        // scaled scores plus mask, in log2 units; keys past S and (causal)
+        // after the row are hidden
+        float mt = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int f = 0; f < 16; ++f) {
+                const int key = k0 + 32 * blk + acc_pos(f, gl);
+                const float mv = float(mraw[blk][(f >> 3) & 1][f & 7]);
+                float sv = fmaf(sacc[blk][f], p.sl2, mv * 1.44269504088896340736f);
+                const bool ok = key < S && (!CAUSAL || key <= qrow);
+                sv = ok ? sv : -INFINITY;
+                sacc[blk][f] = sv;
+                mt = fmaxf(mt, sv);
+            }
+        mt = fmaxf(mt, xor32(mt));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        const float mu = m_new == -INFINITY ? 0.0f : m_new;
+        m_run = m_new;
+        l_run *= alpha;
+        l_ex *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        op_t pop[2][2];  // P operand of block blk, 16-key step kc: registers 8kc .. 8kc+7
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pe = __builtin_amdgcn_exp2f(sacc[blk][8 * kc + e] - mu);
+                    const T pr = static_cast<T>(pe);
+                    l_ex += pe;
+                    l_run += float(pr);
+                    pop[blk][kc][e] = pr;
+                }
+        // Oᵀ += Vᵀ·Pᵀ
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    s16x4 half[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int key = 32 * blk + 16 * kc + 8 * gl + 4 * h + tr_key;
+                        half[h] = lds_read_tr16(vt + key * ROWP + 32 * db + tr_col);
+                    }
+                    const op_t va = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                    oacc[db] = Op<T>::mma(va, pop[blk][kc], oacc[db]);
+                }
+    }
+
+    // O = Oᵀ / l (the sum of the rounded probabilities, over both lane halves),
+    // LSE from the exact sum; a row with no visible key writes zeros and -inf
+    const float l_tot = l_run + xor32(l_run);
+    const float l_e = l_ex + xor32(l_ex);
+    if (live) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        T* orow = static_cast<T*>(p.o) + (int64_t(b) * S + qrow) * qstride + int64_t(hq) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                T vals[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vals[e] = static_cast<T>(oacc[db][8 * h + e] * inv);
+                // head dims 32db + 16h + 8gl .. +7
+                *reinterpret_cast<u32x4*>(orow + 32 * db + 16 * h + 8 * gl) = *reinterpret_cast<const u32x4*>(vals);
+            }
+        if (LSE && gl == 0)
+            p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] =
+                l_e > 0.0f ? (m_run + __builtin_amdgcn_logf(l_e)) * 0.69314718055994530942f : -INFINITY;
+    }
+}
+
+template <typename T, int D, bool CAUSAL, bool LSE>
+int launch_m(const attn_detail::LaunchArgs& a) {
+    MParams mp;
+    mp.q = a.q;
+    mp.k = a.k;
+    mp.v = a.v;
+    mp.mask = a.mask;
+    mp.o = a.o;
+    mp.lse = a.lse;
+    mp.S = int(a.S);
+    mp.Hq = int(a.Hq);
+    mp.Hkv = int(a.Hkv);
+    mp.group = int(a.Hq / a.Hkv);
+    mp.mask_b = a.mask_b;
+    mp.mask_h = a.mask_h;
+    mp.sl2 = a.scale * 1.44269504088896340736f;
+    const unsigned n_qb = unsigned((a.S + kMRows - 1) / kMRows);
+    hipLaunchKernelGGL((masked_kernel<T, D, CAUSAL, LSE>), dim3(n_qb, unsigned(a.Hq), unsigned(a.B)),
+                       dim3(kMThreads), 0, static_cast<hipStream_t>(a.stream), mp);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return ATTN_OK;
+    if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction) return ATTN_ERR_DEVICE;
+    return ATTN_ERR_LAUNCH;
+}
+
+template <typename T, int D>
+int launch_md(const attn_detail::LaunchArgs& a) {
+    if (a.causal) return a.lse ? launch_m<T, D, true, true>(a) : launch_m<T, D, true, false>(a);
+    return a.lse ? launch_m<T, D, false, true>(a) : launch_m<T, D, false, false>(a);
+}
+
+template <typename T>
+int launch_mt(const attn_detail::LaunchArgs& a) {
+    return a.D == 64 ? launch_md<T, 64>(a) : launch_md<T, 128>(a);
+}
+
+}  // namespace
+
+namespace attn_detail {
+
+int launch_masked(const LaunchArgs& a) {
+    return a.dtype == ATTN_BF16 ? launch_mt<__bf16>(a) : launch_mt<_Float16>(a);
+}
+
+}  // namespace attn_detail
