@@ -139,3 +139,15 @@ def test_masked_llama2_7b_layer():
     torch.cuda.synchronize()
     ro, rl = oracle.attention_masked(qn, kn, vn, mn)
     assert_parity(to_np(out), ro, "bf16", lse=l.cpu().numpy(), lse_ref=rl, what="llama2-7b masked")
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,dtype,mshape", [
+    (8, 300, 32, 8, 64, "fp16", "11"),    # 3 query blocks: one pair and one block alone per unit
+    (16, 256, 32, 32, 128, "bf16", "B1"),  # 2 query blocks: one pair per unit
+])
+def test_masked_causal_paired_blocks(B, S, Hq, Hkv, D, dtype, mshape):
+    """Causal launches with at least 512 paired workgroups run the heaviest
+    and the lightest query block in one workgroup."""
+    shape = (1, 1, S, S) if mshape == "11" else (B, 1, S, S)
+    o, l, ro, rl = _run(15 + B, B, S, Hq, Hkv, D, dtype, shape, True)
+    assert_parity(o, ro, dtype, lse=l, lse_ref=rl, what=f"paired B{B} S{S}")

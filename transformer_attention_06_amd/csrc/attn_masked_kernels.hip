@@ -13,13 +13,14 @@
 // MFMA form of the prefill kernel: Sᵀ = K·Qᵀ and Oᵀ += Vᵀ·Pᵀ on 32x32x16
 // MFMA.  Per 64-key tile every lane loads the 32 mask values of its row that
 // its score registers hold (four 16-byte loads: the permuted K order makes
-// them four runs of 8 consecutive keys), K operands come straight from global
-// memory, and the V tile is staged once per workgroup in LDS and read back
-// with the transposing LDS read.  The online softmax keeps fp32 running max
-// and sums per row ("ops-transformer：Transformer算子融合与推理加速实战" §3.2)
-// and rescales the output accumulator whenever the max rises.  Unlike the
-// unmasked kernel this loop is not software-pipelined: every tile reads its
-// own mask block, and the tile loop waits for its loads.
+// them four runs of 8 consecutive keys); the K and V tiles are staged once
+// per workgroup in LDS (V read back with the transposing LDS read), and the
+// next tile's K, V and mask loads are in flight while the current tile is
+// computed ("ops-transformer：Transformer算子融合与推理加速实战" §2.3: prefetch
+// the next block during the current one).  The online softmax keeps fp32
+// running max and sums per row (§3.2) and rescales the output accumulator
+// whenever the max rises.  Unlike the unmasked kernel the MFMAs and the
+// softmax are not interleaved by hand.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -64,7 +65,8 @@ struct MParams {
     const void* mask;  // (Bm, Hm, S, S) in the input type
     void* o;
     float* lse;
-    int S, Hq, Hkv, group;
+    int S, Hq, Hkv, group, n_qb;
+    int pair;  // causal: heavy/light query blocks paired in one workgroup
     int mask_b, mask_h;  // 1 when the mask has a batch (head) dimension of B (Hq)
     float sl2;           // scale * log2(e)
 };
@@ -94,172 +96,196 @@ __global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
     using op_t = typename Op<T>::op_t;
     constexpr int NC = D / 16;                     // MFMA steps along D for Sᵀ
     constexpr int NDB = D / 32;                    // 32-dim blocks of Oᵀ
-    constexpr int ROWP = D + 8;                    // LDS row pitch of the V tile (elements)
+    constexpr int ROWP = D + 8;                    // LDS row pitch of the K and V tiles (elements)
     constexpr int CPR = D / 8;                     // 16-byte chunks per row
     constexpr int NVL = kMKeys * CPR / kMThreads;  // V chunks per thread
     static_assert(NVL * kMThreads == kMKeys * CPR, "V tile split over the workgroup");
     __shared__ __attribute__((aligned(16))) T vt[kMKeys * ROWP];
+    __shared__ __attribute__((aligned(16))) T kt[kMKeys * ROWP];
 
-    // causal: heavy query blocks are dispatched first
-    const int qb = CAUSAL ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
+    // Under causal masking, when the launch is large enough to keep two
+    // workgroups on every CU anyway (p.pair), a workgroup runs two query
+    // blocks one after the other, the heaviest and the lightest remaining
+    // (n_qb-1-i, then i), so every workgroup streams the same number of key
+    // tiles and the last query block does not set the kernel's time alone.
+    // Otherwise one block per workgroup, heaviest first.
+    int nseg = 1, qb0 = CAUSAL ? p.n_qb - 1 - int(blockIdx.x) : int(blockIdx.x), qb1 = -1;
+    if (CAUSAL && p.pair) {
+        qb0 = p.n_qb - 1 - int(blockIdx.x);
+        qb1 = int(blockIdx.x) < qb0 ? int(blockIdx.x) : -1;
+        nseg = qb1 >= 0 ? 2 : 1;
+    }
     const int hq = blockIdx.y, b = blockIdx.z;
     const int g = hq / p.group;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, gl = lane >> 5;
     const int S = p.S;
-    const int q0 = qb * kMRows;
-    const int qrow = q0 + wave * 32 + r;
-    const bool live = qrow < S;
+    for (int sg = 0; sg < nseg; ++sg) {
+        const int qb = sg == 0 ? qb0 : qb1;
+        const int q0 = qb * kMRows;
+        const int qrow = q0 + wave * 32 + r;
+        const bool live = qrow < S;
 
-    const int64_t qstride = int64_t(p.Hq) * D;
-    const int64_t kvstride = int64_t(p.Hkv) * D;
-    const T* kb = static_cast<const T*>(p.k) + int64_t(b) * S * kvstride + int64_t(g) * D;
-    const T* vb = static_cast<const T*>(p.v) + int64_t(b) * S * kvstride + int64_t(g) * D;
-    const int64_t plane = int64_t(p.mask_b ? b : 0) * (p.mask_h ? p.Hq : 1) + (p.mask_h ? hq : 0);
-    const T* mrow = static_cast<const T*>(p.mask) + (plane * S + (live ? qrow : 0)) * int64_t(S);
-    const bool vec_mask = (S & 7) == 0;  // mask rows 16-byte aligned
+        const int64_t qstride = int64_t(p.Hq) * D;
+        const int64_t kvstride = int64_t(p.Hkv) * D;
+        const T* kb = static_cast<const T*>(p.k) + int64_t(b) * S * kvstride + int64_t(g) * D;
+        const T* vb = static_cast<const T*>(p.v) + int64_t(b) * S * kvstride + int64_t(g) * D;
+        const int64_t plane = int64_t(p.mask_b ? b : 0) * (p.mask_h ? p.Hq : 1) + (p.mask_h ? hq : 0);
+        const T* mrow = static_cast<const T*>(p.mask) + (plane * S + (live ? qrow : 0)) * int64_t(S);
+        const bool vec_mask = (S & 7) == 0;  // mask rows 16-byte aligned
 
-    // Q operand: the lane's row, head dims 16c + 8gl .. +7
-    op_t qop[NC];
-    const T* qr = static_cast<const T*>(p.q) + (int64_t(b) * S + qrow) * qstride + int64_t(hq) * D + 8 * gl;
+        // Q operand: the lane's row, head dims 16c + 8gl .. +7
+        op_t qop[NC];
+        const T* qr = static_cast<const T*>(p.q) + (int64_t(b) * S + qrow) * qstride + int64_t(hq) * D + 8 * gl;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qop[c] = live ? *reinterpret_cast<const op_t*>(qr + 16 * c) : op_t{};
+        for (int c = 0; c < NC; ++c) qop[c] = live ? *reinterpret_cast<const op_t*>(qr + 16 * c) : op_t{};
 
-    const int kend = CAUSAL ? (S < q0 + kMRows ? S : q0 + kMRows) : S;
-    const int ntile = (kend + kMKeys - 1) / kMKeys;
-    const int tr_key = (r & 15) >> 2;
-    const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
-    float m_run = -INFINITY, l_run = 0.0f, l_ex = 0.0f;
-    f32x16 oacc[NDB];
+        const int kend = CAUSAL ? (S < q0 + kMRows ? S : q0 + kMRows) : S;
+        const int ntile = (kend + kMKeys - 1) / kMKeys;
+        const int tr_key = (r & 15) >> 2;
+        const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
+        float m_run = -INFINITY, l_run = 0.0f, l_ex = 0.0f;
+        f32x16 oacc[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+        for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
-    for (int t = 0; t < ntile; ++t) {
-        const int k0 = t * kMKeys;
-        // V tile rows (zeros past S), K operands (virtual row r of block blk
-        // is key k0 + 32·blk + perm_row(r)), the lane's mask values
-        u32x4 vreg[NVL];
+        // Tile t+1's V rows, K rows and mask values are loaded into registers
+        // while tile t is computed; at the top of each iteration they go to LDS
+        // (K and V tiles shared by the four wavefronts).  Rows past S are zeros.
+        u32x4 vreg[NVL], kreg[NVL];
+        op_t mnext[2][2];
+        auto load_tile = [&](int t) __attribute__((always_inline)) {
+            const int k0 = t * kMKeys;
 #pragma unroll
-        for (int i = 0; i < NVL; ++i) {
-            const int ch = tid + kMThreads * i, key = k0 + ch / CPR;
-            vreg[i] = key < S ? *reinterpret_cast<const u32x4*>(vb + int64_t(key) * kvstride + 8 * (ch % CPR))
-                              : u32x4{0, 0, 0, 0};
-        }
-        op_t kop[2][NC];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int key = k0 + 32 * blk + perm_row(r);
-            const T* kr = kb + int64_t(key) * kvstride + 8 * gl;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) kop[blk][c] = key < S ? *reinterpret_cast<const op_t*>(kr + 16 * c) : op_t{};
-        }
-        // mask values of keys k0 + 32·blk + 16·h + 8·gl + e (e < 8): the keys
-        // of score registers 8h + e of block blk
-        op_t mraw[2][2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int key0 = k0 + 32 * blk + 16 * h + 8 * gl;
-                if (live && vec_mask && key0 + 8 <= S) {
-                    mraw[blk][h] = *reinterpret_cast<const op_t*>(mrow + key0);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) mraw[blk][h][e] = (live && key0 + e < S) ? mrow[key0 + e] : T(0.0f);
-                }
+            for (int i = 0; i < NVL; ++i) {
+                const int ch = tid + kMThreads * i, key = k0 + ch / CPR;
+                const int64_t off = int64_t(key) * kvstride + 8 * (ch % CPR);
+                vreg[i] = key < S ? *reinterpret_cast<const u32x4*>(vb + off) : u32x4{0, 0, 0, 0};
+                kreg[i] = key < S ? *reinterpret_cast<const u32x4*>(kb + off) : u32x4{0, 0, 0, 0};
             }
-        __syncthreads();  // every wavefront is done reading the previous V tile
+            // mask values of keys k0 + 32·blk + 16·h + 8·gl + e (e < 8): the keys
+            // of score registers 8h + e of block blk
 #pragma unroll
-        for (int i = 0; i < NVL; ++i) {
-            const int ch = tid + kMThreads * i;
-            *reinterpret_cast<u32x4*>(vt + (ch / CPR) * ROWP + 8 * (ch % CPR)) = vreg[i];
-        }
-        __syncthreads();  // the V tile is in place
-
-        // Sᵀ = K·Qᵀ
-        f32x16 sacc[2];
+            for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            sacc[blk] = f32x16{};
+                for (int h = 0; h < 2; ++h) {
+                    const int key0 = k0 + 32 * blk + 16 * h + 8 * gl;
+                    if (live && vec_mask && key0 + 8 <= S) {
+                        mnext[blk][h] = *reinterpret_cast<const op_t*>(mrow + key0);
+                    } else {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) sacc[blk] = Op<T>::mma(kop[blk][c], qop[c], sacc[blk]);
-        }
-        // scaled scores plus mask, in log2 units; keys past S and (causal)
-        // after the row are hidden
-        float mt = -INFINITY;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int f = 0; f < 16; ++f) {
-                const int key = k0 + 32 * blk + acc_pos(f, gl);
-                const float mv = float(mraw[blk][(f >> 3) & 1][f & 7]);
-                float sv = fmaf(sacc[blk][f], p.sl2, mv * 1.44269504088896340736f);
-                const bool ok = key < S && (!CAUSAL || key <= qrow);
-                sv = ok ? sv : -INFINITY;
-                sacc[blk][f] = sv;
-                mt = fmaxf(mt, sv);
-            }
-        mt = fmaxf(mt, xor32(mt));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        const float mu = m_new == -INFINITY ? 0.0f : m_new;
-        m_run = m_new;
-        l_run *= alpha;
-        l_ex *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-        op_t pop[2][2];  // P operand of block blk, 16-key step kc: registers 8kc .. 8kc+7
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(sacc[blk][8 * kc + e] - mu);
-                    const T pr = static_cast<T>(pe);
-                    l_ex += pe;
-                    l_run += float(pr);
-                    pop[blk][kc][e] = pr;
-                }
-        // Oᵀ += Vᵀ·Pᵀ
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    s16x4 half[2];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int key = 32 * blk + 16 * kc + 8 * gl + 4 * h + tr_key;
-                        half[h] = lds_read_tr16(vt + key * ROWP + 32 * db + tr_col);
+                        for (int e = 0; e < 8; ++e) mnext[blk][h][e] = (live && key0 + e < S) ? mrow[key0 + e] : T(0.0f);
                     }
-                    const op_t va = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[db] = Op<T>::mma(va, pop[blk][kc], oacc[db]);
                 }
-    }
-
-    // O = Oᵀ / l (the sum of the rounded probabilities, over both lane halves),
-    // LSE from the exact sum; a row with no visible key writes zeros and -inf
-    const float l_tot = l_run + xor32(l_run);
-    const float l_e = l_ex + xor32(l_ex);
-    if (live) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        T* orow = static_cast<T*>(p.o) + (int64_t(b) * S + qrow) * qstride + int64_t(hq) * D;
+        };
+        if (ntile > 0) load_tile(0);
+        for (int t = 0; t < ntile; ++t) {
+            const int k0 = t * kMKeys;
+            __syncthreads();  // every wavefront is done reading the previous K and V tiles
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                T vals[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vals[e] = static_cast<T>(oacc[db][8 * h + e] * inv);
-                // head dims 32db + 16h + 8gl .. +7
-                *reinterpret_cast<u32x4*>(orow + 32 * db + 16 * h + 8 * gl) = *reinterpret_cast<const u32x4*>(vals);
+            for (int i = 0; i < NVL; ++i) {
+                const int ch = tid + kMThreads * i;
+                const int li = (ch / CPR) * ROWP + 8 * (ch % CPR);
+                *reinterpret_cast<u32x4*>(vt + li) = vreg[i];
+                *reinterpret_cast<u32x4*>(kt + li) = kreg[i];
             }
-        if (LSE && gl == 0)
-            p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] =
-                l_e > 0.0f ? (m_run + __builtin_amdgcn_logf(l_e)) * 0.69314718055994530942f : -INFINITY;
+            op_t mraw[2][2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) mraw[blk][h] = mnext[blk][h];
+            __syncthreads();  // the tiles are in place
+            if (t + 1 < ntile) load_tile(t + 1);
+
+            // K operands from LDS: virtual row r of block blk is key 32·blk +
+            // perm_row(r) of the tile, head dims 16c + 8gl .. +7
+            const T* krow[2] = {kt + perm_row(r) * ROWP + 8 * gl, kt + (32 + perm_row(r)) * ROWP + 8 * gl};
+            // Sᵀ = K·Qᵀ
+            f32x16 sacc[2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                sacc[blk] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    sacc[blk] = Op<T>::mma(*reinterpret_cast<const op_t*>(krow[blk] + 16 * c), qop[c], sacc[blk]);
+            }
+            // scaled scores plus mask, in log2 units; keys past S and (causal)
+            // after the row are hidden
+            float mt = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int f = 0; f < 16; ++f) {
+                    const int key = k0 + 32 * blk + acc_pos(f, gl);
+                    const float mv = float(mraw[blk][(f >> 3) & 1][f & 7]);
+                    float sv = fmaf(sacc[blk][f], p.sl2, mv * 1.44269504088896340736f);
+                    const bool ok = key < S && (!CAUSAL || key <= qrow);
+                    sv = ok ? sv : -INFINITY;
+                    sacc[blk][f] = sv;
+                    mt = fmaxf(mt, sv);
+                }
+            mt = fmaxf(mt, xor32(mt));
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            const float mu = m_new == -INFINITY ? 0.0f : m_new;
+            m_run = m_new;
+            l_run *= alpha;
+            l_ex *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            op_t pop[2][2];  // P operand of block blk, 16-key step kc: registers 8kc .. 8kc+7
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pe = __builtin_amdgcn_exp2f(sacc[blk][8 * kc + e] - mu);
+                        const T pr = static_cast<T>(pe);
+                        l_ex += pe;
+                        l_run += float(pr);
+                        pop[blk][kc][e] = pr;
+                    }
+            // Oᵀ += Vᵀ·Pᵀ
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        s16x4 half[2];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int key = 32 * blk + 16 * kc + 8 * gl + 4 * h + tr_key;
+                            half[h] = lds_read_tr16(vt + key * ROWP + 32 * db + tr_col);
+                        }
+                        const op_t va = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                        oacc[db] = Op<T>::mma(va, pop[blk][kc], oacc[db]);
+                    }
+        }
+
+        // O = Oᵀ / l (the sum of the rounded probabilities, over both lane halves),
+        // LSE from the exact sum; a row with no visible key writes zeros and -inf
+        const float l_tot = l_run + xor32(l_run);
+        const float l_e = l_ex + xor32(l_ex);
+        if (live) {
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            T* orow = static_cast<T*>(p.o) + (int64_t(b) * S + qrow) * qstride + int64_t(hq) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    T vals[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) vals[e] = static_cast<T>(oacc[db][8 * h + e] * inv);
+                    // head dims 32db + 16h + 8gl .. +7
+                    *reinterpret_cast<u32x4*>(orow + 32 * db + 16 * h + 8 * gl) = *reinterpret_cast<const u32x4*>(vals);
+                }
+            if (LSE && gl == 0)
+                p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] =
+                    l_e > 0.0f ? (m_run + __builtin_amdgcn_logf(l_e)) * 0.69314718055994530942f : -INFINITY;
+        }
     }
 }
 
@@ -279,8 +305,14 @@ int launch_m(const attn_detail::LaunchArgs& a) {
     mp.mask_b = a.mask_b;
     mp.mask_h = a.mask_h;
     mp.sl2 = a.scale * 1.44269504088896340736f;
-    const unsigned n_qb = unsigned((a.S + kMRows - 1) / kMRows);
-    hipLaunchKernelGGL((masked_kernel<T, D, CAUSAL, LSE>), dim3(n_qb, unsigned(a.Hq), unsigned(a.B)),
+    mp.n_qb = int((a.S + kMRows - 1) / kMRows);
+    // pair heavy and light causal blocks only when the paired launch still
+    // has two workgroups for each of the 256 CUs: below that, two resident
+    // workgroups per CU (one wavefront of each per SIMD) hide more of the
+    // per-tile load latency than the balance gains
+    mp.pair = CAUSAL && int64_t((mp.n_qb + 1) / 2) * a.Hq * a.B >= 512 ? 1 : 0;
+    const unsigned n_x = unsigned(mp.pair ? (mp.n_qb + 1) / 2 : mp.n_qb);
+    hipLaunchKernelGGL((masked_kernel<T, D, CAUSAL, LSE>), dim3(n_x, unsigned(a.Hq), unsigned(a.B)),
                        dim3(kMThreads), 0, static_cast<hipStream_t>(a.stream), mp);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return ATTN_OK;
