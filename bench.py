@@ -16,6 +16,7 @@ a bounded sample of heads of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--all] [--sweep] [--rope] [--decode] [--varlen] [--masked]
+                    [--general-d]
                     [--copy-calibration]
 """
 
@@ -415,6 +416,9 @@ def main():
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
     ap.add_argument("--decode", action="store_true",
                     help="decode attention over a KV cache (attn_fwd_decode), Llama-2-70B shapes, HBM roofline")
+    ap.add_argument("--general-d", action="store_true",
+                    help="head dims served by the general kernel (D = 80, 96, 160, 256) at B=1, H=32, S=2048, "
+                         "bf16, causal; D = 128 (the tuned kernel) for reference")
     ap.add_argument("--masked", action="store_true",
                     help="additive mask tensor (attn_fwd_masked) on the Llama-2-7B-shaped prefill")
     ap.add_argument("--varlen", action="store_true",
@@ -442,6 +446,15 @@ def main():
     if args.decode:
         for name in DECODE_SHAPES:
             print(json.dumps(bench_decode(name, args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)
+        return
+    if args.general_d:
+        from transformer_attention_06_amd import workloads as W
+        for D in (80, 96, 128, 160, 256):
+            w = W.Workload(f"llama2_7b_prefill_d{D}", 1, B=1, S=2048, Hq=32, Hkv=32, D=D, dtype="bf16", causal=True)
+            W.WORKLOADS[w.name] = w
+            line = bench_one(w.name, args.steps, args.warmup, False, not args.no_graph, warmup_s)
+            line["config"]["kernel"] = "tuned (D = 64, 128)" if D in (64, 128) else "general"
+            print(json.dumps(line), flush=True)
         return
     if args.masked:
         print(json.dumps(bench_masked(args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)

@@ -37,9 +37,13 @@
  *     so an error return leaves the device untouched.  B == 0 or S == 0
  *     returns ATTN_OK without a launch ("ops-transformer…" §6.4: empty input).
  *   - Supported: dtype fp32, fp16, bf16 (q, k, v and out all the same);
- *     D in {64, 128} (the page "CANN-ops-transformer和ATB-昇腾NPU上算子和加速库
- *     怎么配合" gates its fused kernel on head_dim; other D return
- *     ATTN_ERR_UNSUPPORTED: there is no fallback path).
+ *     D in {64, 128} on every entry point.  The page "CANN-ops-transformer和
+ *     ATB-昇腾NPU上算子和加速库怎么配合" gates its fused kernel on a head_dim
+ *     that is a multiple of 16: attn_fwd and attn_fwd_masked also take fp16 /
+ *     bf16 with D a multiple of 16 in [16, 256] (a second, general kernel:
+ *     the head dim padded to a multiple of 32 in registers and LDS, not in
+ *     memory; B <= 65535).  Other D return ATTN_ERR_UNSUPPORTED: there is no
+ *     fallback path.
  *   - Precision: 16-bit inputs run both products on bf16/fp16 MFMA with fp32
  *     accumulation; the running max, running sum and output accumulator are
  *     fp32 and the output is rounded to the input dtype only at the end
@@ -182,8 +186,8 @@ int attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k, const attn_t
  *   q, k, v, scale, causal, n_q_heads, n_kv_heads, out, lse, stream: as for
  *               attn_fwd (no key-padding argument: a mask expresses it).
  *
- * Supported: bf16 and fp16 (fp32 returns ATTN_ERR_UNSUPPORTED), D in {64,
- * 128}, B <= 65535.  One launch; all checks precede it.
+ * Supported: bf16 and fp16 (fp32 returns ATTN_ERR_UNSUPPORTED), D a
+ * multiple of 16 in [16, 256], B <= 65535.  One launch; all checks precede it.
  */
 int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
                     const void* mask, int64_t mask_B, int64_t mask_H, float scale, int causal,

@@ -102,9 +102,18 @@ def test_dtype_checks(lib):
     assert call(lib, T(), T(), T(), T(dtype=A.ATTN_F32)) == A.ATTN_ERR_DTYPE
 
 
-@pytest.mark.parametrize("d", [1, 16, 32, 80, 96, 256])
+@pytest.mark.parametrize("d", [1, 8, 24, 72, 264, 272, 512])
 def test_unsupported_head_dim(lib, d):
     assert call(lib, T(D=d), T(D=d), T(D=d), T(D=d)) == A.ATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("d", [16, 32, 80, 96, 256])
+def test_general_head_dim_16_bit_only(lib, d):
+    # accepted for fp16/bf16 (the general kernel); fp32 keeps D in {64, 128}
+    f32 = dict(dtype=A.ATTN_F32)
+    assert call(lib, T(D=d, **f32), T(D=d, **f32), T(D=d, **f32), T(D=d, **f32)) == A.ATTN_ERR_UNSUPPORTED
+    # a bf16 call with D = d passes every check (caught here on the null data pointer instead of a launch)
+    assert call(lib, T(D=d, data=0), T(D=d), T(D=d), T(D=d)) == A.ATTN_ERR_NULL
 
 
 def test_mask_checks(lib):
@@ -292,8 +301,10 @@ def test_masked_checks(lib):
     assert call_mask(lib, q, k, v, o, mask=FAKE + 8) == A.ATTN_ERR_ALIGN
     assert call_mask(lib, q, k, v, o, causal=2) == A.ATTN_ERR_MASK
     assert call_mask(lib, q, T(B=2, H=3), T(B=2, H=3), o) == A.ATTN_ERR_HEADS
-    assert call_mask(lib, T(B=2, H=4, D=96), T(B=2, H=2, D=96), T(B=2, H=2, D=96),
-                     T(B=2, H=4, D=96)) == A.ATTN_ERR_UNSUPPORTED
+    assert call_mask(lib, T(B=2, H=4, D=72), T(B=2, H=2, D=72), T(B=2, H=2, D=72),
+                     T(B=2, H=4, D=72)) == A.ATTN_ERR_UNSUPPORTED              # not a multiple of 16
+    assert call_mask(lib, T(B=2, H=4, D=272), T(B=2, H=2, D=272), T(B=2, H=2, D=272),
+                     T(B=2, H=4, D=272)) == A.ATTN_ERR_UNSUPPORTED             # above 256
 
 
 def test_masked_empty_returns_ok_without_launch(lib):

@@ -1,0 +1,93 @@
+"""Head dims other than 64 and 128 (multiples of 16 up to 256, fp16/bf16):
+attn_fwd and attn_fwd_masked run them on the general kernel, which pads the
+head dim to a multiple of 32 in registers and LDS only.  Every case is
+checked against the fp64 oracle: padded dims must neither leak into the
+scores nor be written (out is pre-filled with a sentinel in the guard test).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TORCH_DT, prep, to_np
+from tolerances import assert_parity
+from transformer_attention_06_amd import attn as A
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, B, S, Hq, Hkv, D, dtype):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    qd, qn = prep(q, dtype)
+    kd, kn = prep(k, dtype)
+    vd, vn = prep(v, dtype)
+    return (qd, kd, vd), (qn, kn, vn)
+
+
+CASES = [
+    # seed, D, dtype, B, S, Hq, Hkv, causal, pad
+    (1, 16, "bf16", 2, 200, 4, 2, True, None),
+    (2, 32, "fp16", 2, 130, 2, 2, False, [130, 7]),
+    (3, 48, "bf16", 1, 300, 3, 1, True, None),
+    (4, 80, "fp16", 2, 257, 4, 4, True, [100, 257]),
+    (5, 96, "bf16", 1, 77, 6, 2, False, None),
+    (6, 112, "fp16", 1, 129, 2, 1, True, None),
+    (7, 160, "bf16", 2, 200, 2, 2, False, [0, 150]),
+    (8, 192, "fp16", 1, 256, 4, 2, True, None),
+    (9, 224, "bf16", 1, 65, 2, 2, True, None),
+    (10, 256, "bf16", 2, 190, 4, 1, True, [190, 33]),
+    (11, 256, "fp16", 1, 1, 2, 2, False, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"D{c[1]}-{c[2]}-S{c[4]}-c{int(c[7])}")
+def test_general_head_dim(case):
+    seed, D, dtype, B, S, Hq, Hkv, causal, pad = case
+    dev, host = _inputs(seed, B, S, Hq, Hkv, D, dtype)
+    print(f"general-D case seed={seed} D{D} {dtype} B{B} S{S} H{Hq}/{Hkv} causal={causal} pad={pad}", flush=True)
+    pad_d = None if pad is None else torch.from_numpy(np.asarray(pad, np.int32)).cuda()
+    out, lse = A.flash_attention(*dev, causal=causal, pad_lens=pad_d, return_lse=True)
+    torch.cuda.synchronize()
+    mk = oracle.MASK_NONE if pad is None else oracle.MASK_KEY_PADDING
+    ro, rl = oracle.attention(*host, causal=causal, mask_kind=mk, pad_lens=pad)
+    assert_parity(to_np(out), ro, dtype, lse=lse.cpu().numpy(), lse_ref=rl, what=f"D{D}")
+
+
+@pytest.mark.parametrize("D", [80, 256])
+def test_general_head_dim_masked(D):
+    """The mask tensor path at a head dim the tuned kernel does not take."""
+    B, S, Hq, Hkv = 2, 150, 4, 2
+    dev, host = _inputs(20 + D, B, S, Hq, Hkv, D, "bf16")
+    rng = np.random.default_rng(D)
+    m = (rng.standard_normal((B, 1, S, S)) * 2).astype(np.float32)
+    m[rng.random(m.shape) < 0.3] = -np.inf
+    md, mn = prep(m, "bf16")
+    print(f"general-D masked case D{D}", flush=True)
+    out, lse = A.masked_attention(*dev, md, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_masked(*host, mn, causal=True)
+    assert_parity(to_np(out), ro, "bf16", lse=lse.cpu().numpy(), lse_ref=rl, what=f"masked D{D}")
+
+
+def test_general_head_dim_writes_only_its_rows():
+    """D = 80 in a buffer row of 80: the output tensor beyond each head's 80
+    dims belongs to the next head, so a sentinel-filled out must hold only
+    attention values (no write past a row) and match the oracle."""
+    B, S, Hq, Hkv, D = 1, 100, 3, 3, 80
+    dev, host = _inputs(30, B, S, Hq, Hkv, D, "fp16")
+    out = torch.full_like(dev[0], 7.0)
+    print("general-D sentinel case", flush=True)
+    A.attn_fwd(*dev, A.ATTN_MASK_NONE, None, None, False, Hq, Hkv, out, None)
+    torch.cuda.synchronize()
+    ro, _ = oracle.attention(*host)
+    assert_parity(to_np(out), ro, "fp16", what="sentinel D80")
+
+
+def test_general_head_dim_fp32_rejected():
+    q = torch.zeros((1, 8, 2, 96), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        A.flash_attention(q, q, q)

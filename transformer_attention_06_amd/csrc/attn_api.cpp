@@ -20,9 +20,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Checks every argument of attn_fwd and fills the launch struct; `empty` is
 // set when there is nothing to launch (B == 0 or S == 0).
+// general_d: head dims other than 64 and 128 (multiples of 16 up to 256,
+// 16-bit types) are accepted; they run on the general kernel.
 int prepare(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v, int mask_kind,
             const int32_t* pad_lens, float scale, int causal, int n_q_heads, int n_kv_heads,
-            const attn_tensor_t* out, float* lse, void* stream, attn_detail::LaunchArgs& a, bool& empty) {
+            const attn_tensor_t* out, float* lse, void* stream, attn_detail::LaunchArgs& a, bool& empty,
+            bool general_d = false) {
     empty = false;
     if (!q || !k || !v || !out) return ATTN_ERR_NULL;
     if (!valid_dtype(q->dtype) || !valid_dtype(k->dtype) || !valid_dtype(v->dtype) ||
@@ -52,7 +55,9 @@ int prepare(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t*
         return ATTN_ERR_MASK;
     }
 
-    if (q->D != 64 && q->D != 128) return ATTN_ERR_UNSUPPORTED;
+    const bool d_tuned = q->D == 64 || q->D == 128;
+    const bool d_general = general_d && q->dtype != ATTN_F32 && q->D % 16 == 0 && q->D >= 16 && q->D <= 256;
+    if (!d_tuned && !d_general) return ATTN_ERR_UNSUPPORTED;
 
     const int64_t B = q->B, S = q->S, D = q->D;
     if (B == 0 || S == 0) {  // empty input: nothing to launch
@@ -116,9 +121,13 @@ extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const at
     attn_detail::LaunchArgs a;
     bool empty = false;
     const int rc = prepare(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
-                           stream, a, empty);
+                           stream, a, empty, true);
     if (rc != ATTN_OK || empty) return rc;
-    return attn_detail::launch(a);
+    if (a.D == 64 || a.D == 128) return attn_detail::launch(a);
+    // other head dims: the general kernel (one workgroup per batch, head and
+    // 128-row block; batch on the grid's z axis)
+    if (a.B > 65535) return ATTN_ERR_UNSUPPORTED;
+    return attn_detail::launch_general(a);
 }
 
 // Packed variable-length sequences ([ATB-guide] §6.1 and §8.7: one
@@ -160,7 +169,7 @@ extern "C" int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, c
     attn_detail::LaunchArgs a;
     bool empty = false;
     const int rc = prepare(q, k, v, ATTN_MASK_NONE, nullptr, scale, causal, n_q_heads, n_kv_heads, out, lse,
-                           stream, a, empty);
+                           stream, a, empty, true);
     if (rc != ATTN_OK) return rc;
     if (q->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;  // 16-bit types only
     if (mask_B != 1 && mask_B != q->B) return ATTN_ERR_MASK;
@@ -300,7 +309,7 @@ extern "C" const char* attn_strerror(int code) {
         case ATTN_ERR_SHAPE: return "B, S or D disagree between q, k, v, out (or are negative)";
         case ATTN_ERR_HEADS: return "head counts disagree with the tensors, or n_q_heads % n_kv_heads != 0";
         case ATTN_ERR_DTYPE: return "unknown dtype, or q, k, v, out are not all the same dtype";
-        case ATTN_ERR_UNSUPPORTED: return "unsupported size: D must be 64 or 128, and sizes within the documented limits";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported size or type: D must be 64 or 128 (attn_fwd and attn_fwd_masked: a multiple of 16 in [16, 256] for fp16/bf16), and sizes within the documented limits";
         case ATTN_ERR_MASK: return "bad mask arguments: mask_kind unknown, pad_lens NULL/non-NULL mismatch, or causal not 0/1";
         case ATTN_ERR_ALIGN: return "a data pointer is not 16-byte aligned (pad_lens/lse: 4-byte)";
         case ATTN_ERR_LAUNCH: return "the HIP kernel launch failed";

@@ -44,6 +44,10 @@ int launch(const LaunchArgs& a);
 // Enqueue the attention with an additive mask tensor (16-bit types only).
 int launch_masked(const LaunchArgs& a);
 
+// Enqueue the general kernel (16-bit types; head dims that are multiples of
+// 16 up to 256) without a mask tensor.
+int launch_general(const LaunchArgs& a);
+
 // Enqueue the rotary embedding of K (a.k, layout (B, S, Hkv, D)) into
 // k_out (same layout; may be a.k itself) with a.rope_pos and a.rope_f.
 int launch_rope_k(const LaunchArgs& a, void* k_out);

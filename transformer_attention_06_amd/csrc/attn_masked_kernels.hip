@@ -65,7 +65,8 @@ struct MParams {
     const void* mask;  // (Bm, Hm, S, S) in the input type
     void* o;
     float* lse;
-    int S, Hq, Hkv, group, n_qb;
+    int S, Hq, Hkv, group, n_qb, D;
+    const int32_t* pad_lens;  // key padding (int32[B]) or null
     int pair;  // causal: heavy/light query blocks paired in one workgroup
     int mask_b, mask_h;  // 1 when the mask has a batch (head) dimension of B (Hq)
     float sl2;           // scale * log2(e)
@@ -91,13 +92,18 @@ __device__ __forceinline__ float xor32(float x) {
     return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-template <typename T, int D, bool CAUSAL, bool LSE>
-__global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
+// DP: the head dimension padded to a multiple of 32 (the tile width); the
+// real head dimension p.D (a multiple of 16, at most DP) sets the strides,
+// and head-dim chunks at or past it are read as zeros and not written.
+// MASK: an additive mask tensor is read per tile (else none).  EXACT: D ==
+// DP, known at compile time (no head-dim guards).
+template <typename T, int DP, bool CAUSAL, bool MASK, bool EXACT>
+__global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MParams p) {
     using op_t = typename Op<T>::op_t;
-    constexpr int NC = D / 16;                     // MFMA steps along D for Sᵀ
-    constexpr int NDB = D / 32;                    // 32-dim blocks of Oᵀ
-    constexpr int ROWP = D + 8;                    // LDS row pitch of the K and V tiles (elements)
-    constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    constexpr int NC = DP / 16;                    // MFMA steps along the head dim for Sᵀ
+    constexpr int NDB = DP / 32;                   // 32-dim blocks of Oᵀ
+    constexpr int ROWP = DP + 8;                   // LDS row pitch of the K and V tiles (elements)
+    constexpr int CPR = DP / 8;                    // 16-byte chunks per (padded) row
     constexpr int NVL = kMKeys * CPR / kMThreads;  // V chunks per thread
     static_assert(NVL * kMThreads == kMKeys * CPR, "V tile split over the workgroup");
     __shared__ __attribute__((aligned(16))) T vt[kMKeys * ROWP];
@@ -121,6 +127,12 @@ __global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, gl = lane >> 5;
     const int S = p.S;
+    const int D = EXACT ? DP : p.D;
+    int key_lim = S;  // keys at or past this are hidden (key padding)
+    if (p.pad_lens) {
+        const int L = p.pad_lens[b];
+        key_lim = L < 0 ? 0 : (L > S ? S : L);
+    }
     for (int sg = 0; sg < nseg; ++sg) {
         const int qb = sg == 0 ? qb0 : qb1;
         const int q0 = qb * kMRows;
@@ -132,16 +144,17 @@ __global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
         const T* kb = static_cast<const T*>(p.k) + int64_t(b) * S * kvstride + int64_t(g) * D;
         const T* vb = static_cast<const T*>(p.v) + int64_t(b) * S * kvstride + int64_t(g) * D;
         const int64_t plane = int64_t(p.mask_b ? b : 0) * (p.mask_h ? p.Hq : 1) + (p.mask_h ? hq : 0);
-        const T* mrow = static_cast<const T*>(p.mask) + (plane * S + (live ? qrow : 0)) * int64_t(S);
+        const T* mrow = MASK ? static_cast<const T*>(p.mask) + (plane * S + (live ? qrow : 0)) * int64_t(S) : nullptr;
         const bool vec_mask = (S & 7) == 0;  // mask rows 16-byte aligned
 
         // Q operand: the lane's row, head dims 16c + 8gl .. +7
         op_t qop[NC];
         const T* qr = static_cast<const T*>(p.q) + (int64_t(b) * S + qrow) * qstride + int64_t(hq) * D + 8 * gl;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) qop[c] = live ? *reinterpret_cast<const op_t*>(qr + 16 * c) : op_t{};
+        for (int c = 0; c < NC; ++c)
+            qop[c] = live && 16 * c + 8 * gl < D ? *reinterpret_cast<const op_t*>(qr + 16 * c) : op_t{};
 
-        const int kend = CAUSAL ? (S < q0 + kMRows ? S : q0 + kMRows) : S;
+        const int kend = CAUSAL ? (key_lim < q0 + kMRows ? key_lim : q0 + kMRows) : key_lim;
         const int ntile = (kend + kMKeys - 1) / kMKeys;
         const int tr_key = (r & 15) >> 2;
         const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
@@ -150,36 +163,47 @@ __global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
 
-        // Tile t+1's V rows, K rows and mask values are loaded into registers
-        // while tile t is computed; at the top of each iteration they go to LDS
-        // (K and V tiles shared by the four wavefronts).  Rows past S are zeros.
+        // Tile t+1's V and K rows are loaded into registers while tile t is
+        // computed; at the top of each iteration they go to LDS (K and V
+        // tiles shared by the four wavefronts).  Rows past the valid keys are
+        // zeros.  Tile t+1's mask values are loaded as soon as tile t's
+        // scores have taken theirs (one register set).
         u32x4 vreg[NVL], kreg[NVL];
         op_t mnext[2][2];
         auto load_tile = [&](int t) __attribute__((always_inline)) {
             const int k0 = t * kMKeys;
 #pragma unroll
             for (int i = 0; i < NVL; ++i) {
-                const int ch = tid + kMThreads * i, key = k0 + ch / CPR;
-                const int64_t off = int64_t(key) * kvstride + 8 * (ch % CPR);
-                vreg[i] = key < S ? *reinterpret_cast<const u32x4*>(vb + off) : u32x4{0, 0, 0, 0};
-                kreg[i] = key < S ? *reinterpret_cast<const u32x4*>(kb + off) : u32x4{0, 0, 0, 0};
+                const int ch = tid + kMThreads * i, key = k0 + ch / CPR, col = 8 * (ch % CPR);
+                const int64_t off = int64_t(key) * kvstride + col;
+                const bool in = key < key_lim && col < D;
+                vreg[i] = in ? *reinterpret_cast<const u32x4*>(vb + off) : u32x4{0, 0, 0, 0};
+                kreg[i] = in ? *reinterpret_cast<const u32x4*>(kb + off) : u32x4{0, 0, 0, 0};
             }
-            // mask values of keys k0 + 32·blk + 16·h + 8·gl + e (e < 8): the keys
-            // of score registers 8h + e of block blk
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int key0 = k0 + 32 * blk + 16 * h + 8 * gl;
-                    if (live && vec_mask && key0 + 8 <= S) {
-                        mnext[blk][h] = *reinterpret_cast<const op_t*>(mrow + key0);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) mnext[blk][h][e] = (live && key0 + e < S) ? mrow[key0 + e] : T(0.0f);
-                    }
-                }
         };
-        if (ntile > 0) load_tile(0);
+        // mask values of keys k0 + 32·blk + 16·h + 8·gl + e (e < 8): the keys
+        // of score registers 8h + e of block blk
+        auto load_mask = [&](int t) __attribute__((always_inline)) {
+            const int k0 = t * kMKeys;
+            if constexpr (MASK) {
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int key0 = k0 + 32 * blk + 16 * h + 8 * gl;
+                        if (live && vec_mask && key0 + 8 <= S) {
+                            mnext[blk][h] = *reinterpret_cast<const op_t*>(mrow + key0);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) mnext[blk][h][e] = (live && key0 + e < S) ? mrow[key0 + e] : T(0.0f);
+                        }
+                    }
+            }
+        };
+        if (ntile > 0) {
+            load_tile(0);
+            load_mask(0);
+        }
         for (int t = 0; t < ntile; ++t) {
             const int k0 = t * kMKeys;
             __syncthreads();  // every wavefront is done reading the previous K and V tiles
@@ -190,11 +214,6 @@ __global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
                 *reinterpret_cast<u32x4*>(vt + li) = vreg[i];
                 *reinterpret_cast<u32x4*>(kt + li) = kreg[i];
             }
-            op_t mraw[2][2];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) mraw[blk][h] = mnext[blk][h];
             __syncthreads();  // the tiles are in place
             if (t + 1 < ntile) load_tile(t + 1);
 
@@ -218,14 +237,15 @@ __global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
 #pragma unroll
                 for (int f = 0; f < 16; ++f) {
                     const int key = k0 + 32 * blk + acc_pos(f, gl);
-                    const float mv = float(mraw[blk][(f >> 3) & 1][f & 7]);
-                    float sv = fmaf(sacc[blk][f], p.sl2, mv * 1.44269504088896340736f);
-                    const bool ok = key < S && (!CAUSAL || key <= qrow);
+                    float sv = sacc[blk][f] * p.sl2;
+                    if constexpr (MASK) sv = fmaf(float(mnext[blk][(f >> 3) & 1][f & 7]), 1.44269504088896340736f, sv);
+                    const bool ok = key < key_lim && (!CAUSAL || key <= qrow);
                     sv = ok ? sv : -INFINITY;
                     sacc[blk][f] = sv;
                     mt = fmaxf(mt, sv);
                 }
             mt = fmaxf(mt, xor32(mt));
+            if (MASK && t + 1 < ntile) load_mask(t + 1);  // this tile's mask values are used
             const float m_new = fmaxf(m_run, mt);
             const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             const float mu = m_new == -INFINITY ? 0.0f : m_new;
@@ -280,16 +300,18 @@ __global__ __launch_bounds__(kMThreads, 2) void masked_kernel(MParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) vals[e] = static_cast<T>(oacc[db][8 * h + e] * inv);
                     // head dims 32db + 16h + 8gl .. +7
-                    *reinterpret_cast<u32x4*>(orow + 32 * db + 16 * h + 8 * gl) = *reinterpret_cast<const u32x4*>(vals);
+                    if (32 * db + 16 * h + 8 * gl < D)
+                        *reinterpret_cast<u32x4*>(orow + 32 * db + 16 * h + 8 * gl) =
+                            *reinterpret_cast<const u32x4*>(vals);
                 }
-            if (LSE && gl == 0)
+            if (p.lse && gl == 0)
                 p.lse[(int64_t(b) * p.Hq + hq) * S + qrow] =
                     l_e > 0.0f ? (m_run + __builtin_amdgcn_logf(l_e)) * 0.69314718055994530942f : -INFINITY;
         }
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool LSE>
+template <typename T, int DP, bool CAUSAL, bool MASK, bool EXACT>
 int launch_m(const attn_detail::LaunchArgs& a) {
     MParams mp;
     mp.q = a.q;
@@ -302,6 +324,8 @@ int launch_m(const attn_detail::LaunchArgs& a) {
     mp.Hq = int(a.Hq);
     mp.Hkv = int(a.Hkv);
     mp.group = int(a.Hq / a.Hkv);
+    mp.D = int(a.D);
+    mp.pad_lens = a.padded ? a.pad_lens : nullptr;
     mp.mask_b = a.mask_b;
     mp.mask_h = a.mask_h;
     mp.sl2 = a.scale * 1.44269504088896340736f;
@@ -312,7 +336,7 @@ int launch_m(const attn_detail::LaunchArgs& a) {
     // per-tile load latency than the balance gains
     mp.pair = CAUSAL && int64_t((mp.n_qb + 1) / 2) * a.Hq * a.B >= 512 ? 1 : 0;
     const unsigned n_x = unsigned(mp.pair ? (mp.n_qb + 1) / 2 : mp.n_qb);
-    hipLaunchKernelGGL((masked_kernel<T, D, CAUSAL, LSE>), dim3(n_x, unsigned(a.Hq), unsigned(a.B)),
+    hipLaunchKernelGGL((masked_kernel<T, DP, CAUSAL, MASK, EXACT>), dim3(n_x, unsigned(a.Hq), unsigned(a.B)),
                        dim3(kMThreads), 0, static_cast<hipStream_t>(a.stream), mp);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return ATTN_OK;
@@ -320,15 +344,26 @@ int launch_m(const attn_detail::LaunchArgs& a) {
     return ATTN_ERR_LAUNCH;
 }
 
-template <typename T, int D>
-int launch_md(const attn_detail::LaunchArgs& a) {
-    if (a.causal) return a.lse ? launch_m<T, D, true, true>(a) : launch_m<T, D, true, false>(a);
-    return a.lse ? launch_m<T, D, false, true>(a) : launch_m<T, D, false, false>(a);
+template <typename T, int DP, bool MASK>
+int launch_mc(const attn_detail::LaunchArgs& a) {
+    if (a.D == DP)
+        return a.causal ? launch_m<T, DP, true, MASK, true>(a) : launch_m<T, DP, false, MASK, true>(a);
+    return a.causal ? launch_m<T, DP, true, MASK, false>(a) : launch_m<T, DP, false, MASK, false>(a);
 }
 
-template <typename T>
+// head dim padded to the next multiple of 32 (D is a multiple of 16 in [16, 256])
+template <typename T, bool MASK>
 int launch_mt(const attn_detail::LaunchArgs& a) {
-    return a.D == 64 ? launch_md<T, 64>(a) : launch_md<T, 128>(a);
+    switch ((a.D + 31) / 32) {
+        case 1: return launch_mc<T, 32, MASK>(a);
+        case 2: return launch_mc<T, 64, MASK>(a);
+        case 3: return launch_mc<T, 96, MASK>(a);
+        case 4: return launch_mc<T, 128, MASK>(a);
+        case 5: return launch_mc<T, 160, MASK>(a);
+        case 6: return launch_mc<T, 192, MASK>(a);
+        case 7: return launch_mc<T, 224, MASK>(a);
+        default: return launch_mc<T, 256, MASK>(a);
+    }
 }
 
 }  // namespace
@@ -336,7 +371,11 @@ int launch_mt(const attn_detail::LaunchArgs& a) {
 namespace attn_detail {
 
 int launch_masked(const LaunchArgs& a) {
-    return a.dtype == ATTN_BF16 ? launch_mt<__bf16>(a) : launch_mt<_Float16>(a);
+    return a.dtype == ATTN_BF16 ? launch_mt<__bf16, true>(a) : launch_mt<_Float16, true>(a);
+}
+
+int launch_general(const LaunchArgs& a) {
+    return a.dtype == ATTN_BF16 ? launch_mt<__bf16, false>(a) : launch_mt<_Float16, false>(a);
 }
 
 }  // namespace attn_detail
