@@ -371,30 +371,45 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(DecParams p
     const T* vb = static_cast<const T*>(p.v) + (int64_t(b) * p.Sk * p.Hkv + g) * D;
     T* vw = vt + wave * KW * ROWP;
 
-    // V: the wavefront's 64 cache rows into its LDS tile (zeros past L, so
-    // that a zero probability never meets a stale value)
+    // Loads without branches, so that every load of the wavefront is in
+    // flight at once: cache rows past L are read as row L-1 (their scores
+    // are hidden, so they only meet P = 0), and a wavefront whose 64 keys
+    // all lie past L loads nothing (a wavefront-uniform branch).
+    const bool any = k0 < L;
+    const int klast = L - 1;
+    // V: the wavefront's 64 cache rows into its LDS tile
     u32x4 vreg[NVL];
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-        const int ch = lane + 64 * i, key = k0 + ch / CPR, c8 = ch % CPR;
-        vreg[i] = key < L ? *reinterpret_cast<const u32x4*>(vb + int64_t(key) * kv_row + 8 * c8) : u32x4{0, 0, 0, 0};
-    }
     // K operands: block blk, virtual row r is key k0 + 32·blk + perm_row(r);
     // the lane holds head dims 16c + 8gl .. +7
     op_t kop[2][NC];
+    if (any) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        const int key = k0 + 32 * blk + perm_row(r);
-        const T* kr = kb + int64_t(key) * kv_row + 8 * gl;
+        for (int i = 0; i < NVL; ++i) {
+            const int ch = lane + 64 * i, key = k0 + ch / CPR, c8 = ch % CPR;
+            vreg[i] = *reinterpret_cast<const u32x4*>(vb + int64_t(key < L ? key : klast) * kv_row + 8 * c8);
+        }
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            kop[blk][c] = key < L ? *reinterpret_cast<const op_t*>(kr + 16 * c) : op_t{};
+        for (int blk = 0; blk < 2; ++blk) {
+            const int key = k0 + 32 * blk + perm_row(r);
+            const T* kr = kb + int64_t(key < L ? key : klast) * kv_row + 8 * gl;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) kop[blk][c] = *reinterpret_cast<const op_t*>(kr + 16 * c);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NVL; ++i) vreg[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) kop[blk][c] = op_t{};
     }
-    // Q operand: the lane's row, head dims 16c + 8gl .. +7
+    // Q operand: the lane's row, head dims 16c + 8gl .. +7 (rows past the
+    // group read the group's first row: their keys are all hidden and their
+    // results are never written)
     op_t qop[NC];
     const T* qr = static_cast<const T*>(p.q) + ((int64_t(b) * p.Sq + tok) * p.Hq + hq) * D + 8 * gl;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qop[c] = live ? *reinterpret_cast<const op_t*>(qr + 16 * c) : op_t{};
+    for (int c = 0; c < NC; ++c) qop[c] = *reinterpret_cast<const op_t*>(qr + 16 * c);
 
 #pragma unroll
     for (int i = 0; i < NVL; ++i) {

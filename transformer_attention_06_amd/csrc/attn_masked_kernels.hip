@@ -95,11 +95,14 @@ __device__ __forceinline__ float xor32(float x) {
 // DP: the head dimension padded to a multiple of 32 (the tile width); the
 // real head dimension p.D (a multiple of 16, at most DP) sets the strides,
 // and head-dim chunks at or past it are read as zeros and not written.
-// MASK: an additive mask tensor is read per tile (else none).  EXACT: D ==
-// DP, known at compile time (no head-dim guards).
-template <typename T, int DP, bool CAUSAL, bool MASK, bool EXACT>
+// MK: 0 no mask tensor; 1 an additive mask tensor whose rows are 16-byte
+// aligned (S a multiple of 8: 16-byte loads); 2 the same with unaligned rows
+// (element loads).  EXACT: D == DP, known at compile time (no head-dim
+// guards).
+template <typename T, int DP, bool CAUSAL, int MK, bool EXACT>
 __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MParams p) {
     using op_t = typename Op<T>::op_t;
+    constexpr bool MASK = MK != 0;
     constexpr int NC = DP / 16;                    // MFMA steps along the head dim for Sᵀ
     constexpr int NDB = DP / 32;                   // 32-dim blocks of Oᵀ
     constexpr int ROWP = DP + 8;                   // LDS row pitch of the K and V tiles (elements)
@@ -145,14 +148,20 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
         const T* vb = static_cast<const T*>(p.v) + int64_t(b) * S * kvstride + int64_t(g) * D;
         const int64_t plane = int64_t(p.mask_b ? b : 0) * (p.mask_h ? p.Hq : 1) + (p.mask_h ? hq : 0);
         const T* mrow = MASK ? static_cast<const T*>(p.mask) + (plane * S + (live ? qrow : 0)) * int64_t(S) : nullptr;
-        const bool vec_mask = (S & 7) == 0;  // mask rows 16-byte aligned
 
         // Q operand: the lane's row, head dims 16c + 8gl .. +7
         op_t qop[NC];
-        const T* qr = static_cast<const T*>(p.q) + (int64_t(b) * S + qrow) * qstride + int64_t(hq) * D + 8 * gl;
+        const T* qr = static_cast<const T*>(p.q) + (int64_t(b) * S + (live ? qrow : S - 1)) * qstride +
+                      int64_t(hq) * D + 8 * gl;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            qop[c] = live && 16 * c + 8 * gl < D ? *reinterpret_cast<const op_t*>(qr + 16 * c) : op_t{};
+        for (int c = 0; c < NC; ++c) {
+            // unconditional load from a valid address (row S-1 for rows past
+            // S, whose results are never written; chunk 0 for head-dim chunks
+            // past D, zeroed by the select): no branch, all loads in flight
+            const bool in_d = EXACT || 16 * c + 8 * gl < D;
+            const op_t x = *reinterpret_cast<const op_t*>(qr + (in_d ? 16 * c : 0));
+            qop[c] = in_d ? x : op_t{};
+        }
 
         const int kend = CAUSAL ? (key_lim < q0 + kMRows ? key_lim : q0 + kMRows) : key_lim;
         const int ntile = (kend + kMKeys - 1) / kMKeys;
@@ -170,15 +179,25 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
         // scores have taken theirs (one register set).
         u32x4 vreg[NVL], kreg[NVL];
         op_t mnext[2][2];
+        const int nrec = key_lim > 0 ? int((int64_t(key_lim) * kvstride - int64_t(g) * D) * int64_t(sizeof(T))) : 0;
+        const __amdgpu_buffer_rsrc_t krs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(kb), 0, nrec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vrs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(vb), 0, nrec, 0x00020000);
         auto load_tile = [&](int t) __attribute__((always_inline)) {
             const int k0 = t * kMKeys;
 #pragma unroll
             for (int i = 0; i < NVL; ++i) {
+                // buffer loads over rows [0, key_lim) of this (batch, kv head):
+                // rows past it, and head-dim chunks past D (given an offset
+                // past the range), read as zeros without touching memory; no
+                // branch, so every load is in flight together (byte offsets
+                // fit 32 bits: S·Hkv·D·elt < 2^31 is checked on the host)
                 const int ch = tid + kMThreads * i, key = k0 + ch / CPR, col = 8 * (ch % CPR);
-                const int64_t off = int64_t(key) * kvstride + col;
-                const bool in = key < key_lim && col < D;
-                vreg[i] = in ? *reinterpret_cast<const u32x4*>(vb + off) : u32x4{0, 0, 0, 0};
-                kreg[i] = in ? *reinterpret_cast<const u32x4*>(kb + off) : u32x4{0, 0, 0, 0};
+                const bool in_d = EXACT || col < D;
+                const int boff = in_d ? int((int64_t(key) * kvstride + col) * int64_t(sizeof(T))) : 0x7ffffff0;
+                vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, boff, 0, 0));
+                kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, boff, 0, 0));
             }
         };
         // mask values of keys k0 + 32·blk + 16·h + 8·gl + e (e < 8): the keys
@@ -190,12 +209,16 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
                 for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
+                        // addresses clamped into the row (keys at or past S are
+                        // hidden anyway; with S a multiple of 8 a run of 8 is
+                        // either inside or wholly past S); rows past S read
+                        // row 0 of the plane (never written out)
                         const int key0 = k0 + 32 * blk + 16 * h + 8 * gl;
-                        if (live && vec_mask && key0 + 8 <= S) {
-                            mnext[blk][h] = *reinterpret_cast<const op_t*>(mrow + key0);
+                        if constexpr (MK == 1) {
+                            mnext[blk][h] = *reinterpret_cast<const op_t*>(mrow + (key0 + 8 <= S ? key0 : S - 8));
                         } else {
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) mnext[blk][h][e] = (live && key0 + e < S) ? mrow[key0 + e] : T(0.0f);
+                            for (int e = 0; e < 8; ++e) mnext[blk][h][e] = mrow[key0 + e < S ? key0 + e : S - 1];
                         }
                     }
             }
@@ -311,7 +334,7 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
     }
 }
 
-template <typename T, int DP, bool CAUSAL, bool MASK, bool EXACT>
+template <typename T, int DP, bool CAUSAL, int MK, bool EXACT>
 int launch_m(const attn_detail::LaunchArgs& a) {
     MParams mp;
     mp.q = a.q;
@@ -336,7 +359,7 @@ int launch_m(const attn_detail::LaunchArgs& a) {
     // per-tile load latency than the balance gains
     mp.pair = CAUSAL && int64_t((mp.n_qb + 1) / 2) * a.Hq * a.B >= 512 ? 1 : 0;
     const unsigned n_x = unsigned(mp.pair ? (mp.n_qb + 1) / 2 : mp.n_qb);
-    hipLaunchKernelGGL((masked_kernel<T, DP, CAUSAL, MASK, EXACT>), dim3(n_x, unsigned(a.Hq), unsigned(a.B)),
+    hipLaunchKernelGGL((masked_kernel<T, DP, CAUSAL, MK, EXACT>), dim3(n_x, unsigned(a.Hq), unsigned(a.B)),
                        dim3(kMThreads), 0, static_cast<hipStream_t>(a.stream), mp);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return ATTN_OK;
@@ -344,25 +367,31 @@ int launch_m(const attn_detail::LaunchArgs& a) {
     return ATTN_ERR_LAUNCH;
 }
 
-template <typename T, int DP, bool MASK>
+template <typename T, int DP, int MK>
 int launch_mc(const attn_detail::LaunchArgs& a) {
     if (a.D == DP)
-        return a.causal ? launch_m<T, DP, true, MASK, true>(a) : launch_m<T, DP, false, MASK, true>(a);
-    return a.causal ? launch_m<T, DP, true, MASK, false>(a) : launch_m<T, DP, false, MASK, false>(a);
+        return a.causal ? launch_m<T, DP, true, MK, true>(a) : launch_m<T, DP, false, MK, true>(a);
+    return a.causal ? launch_m<T, DP, true, MK, false>(a) : launch_m<T, DP, false, MK, false>(a);
+}
+
+template <typename T, int DP, bool MASK>
+int launch_mk(const attn_detail::LaunchArgs& a) {
+    if (!MASK) return launch_mc<T, DP, 0>(a);
+    return a.S % 8 == 0 ? launch_mc<T, DP, 1>(a) : launch_mc<T, DP, 2>(a);
 }
 
 // head dim padded to the next multiple of 32 (D is a multiple of 16 in [16, 256])
 template <typename T, bool MASK>
 int launch_mt(const attn_detail::LaunchArgs& a) {
     switch ((a.D + 31) / 32) {
-        case 1: return launch_mc<T, 32, MASK>(a);
-        case 2: return launch_mc<T, 64, MASK>(a);
-        case 3: return launch_mc<T, 96, MASK>(a);
-        case 4: return launch_mc<T, 128, MASK>(a);
-        case 5: return launch_mc<T, 160, MASK>(a);
-        case 6: return launch_mc<T, 192, MASK>(a);
-        case 7: return launch_mc<T, 224, MASK>(a);
-        default: return launch_mc<T, 256, MASK>(a);
+        case 1: return launch_mk<T, 32, MASK>(a);
+        case 2: return launch_mk<T, 64, MASK>(a);
+        case 3: return launch_mk<T, 96, MASK>(a);
+        case 4: return launch_mk<T, 128, MASK>(a);
+        case 5: return launch_mk<T, 160, MASK>(a);
+        case 6: return launch_mk<T, 192, MASK>(a);
+        case 7: return launch_mk<T, 224, MASK>(a);
+        default: return launch_mk<T, 256, MASK>(a);
     }
 }
 
