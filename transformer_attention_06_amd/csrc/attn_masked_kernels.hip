@@ -99,22 +99,40 @@ __device__ __forceinline__ float xor32(float x) {
 // aligned (S a multiple of 8: 16-byte loads); 2 the same with unaligned rows
 // (element loads).  EXACT: D == DP, known at compile time (no head-dim
 // guards).
+//
+// Head dims up to 128 run two groups of four wavefronts per workgroup (NG =
+// 2): both groups take the same query block, group 0 its first half of the
+// key tiles and group 1 the second half, each with its own LDS tiles, and
+// the two partial softmax states (m, l, O) are merged through LDS at the end
+// of the block ("ops-transformer…" §3.2's recurrence applied to two key
+// ranges).  Wider head dims run one group (their registers need one
+// wavefront per SIMD).
+template <int DP>
+struct MGroups {
+    static constexpr int value = DP <= 128 ? 2 : 1;
+};
+
 template <typename T, int DP, bool CAUSAL, int MK, bool EXACT>
-__global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MParams p) {
+__global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kernel(MParams p) {
     using op_t = typename Op<T>::op_t;
     constexpr bool MASK = MK != 0;
+    constexpr int NG = MGroups<DP>::value;
     constexpr int NC = DP / 16;                    // MFMA steps along the head dim for Sᵀ
     constexpr int NDB = DP / 32;                   // 32-dim blocks of Oᵀ
     constexpr int ROWP = DP + 8;                   // LDS row pitch of the K and V tiles (elements)
     constexpr int CPR = DP / 8;                    // 16-byte chunks per (padded) row
     constexpr int NVL = kMKeys * CPR / kMThreads;  // V chunks per thread
-    static_assert(NVL * kMThreads == kMKeys * CPR, "V tile split over the workgroup");
-    __shared__ __attribute__((aligned(16))) T vt[kMKeys * ROWP];
-    __shared__ __attribute__((aligned(16))) T kt[kMKeys * ROWP];
+    static_assert(NVL * kMThreads == kMKeys * CPR, "V tile split over a group");
+    constexpr int TILE = kMKeys * ROWP;            // elements per K (or V) tile
+    // per group: V tile, then K tile; after a block the region holds group
+    // 1's partial output for the merge
+    __shared__ __attribute__((aligned(16))) T lds[NG * 2 * TILE];
+    __shared__ float s_ml[4][3][64];
+    static_assert(NG == 1 || 4 * (DP / 32) * 16 * 64 * 4 <= int(sizeof(lds)), "merge stash fits the tiles");
 
-    // Under causal masking, when the launch is large enough to keep two
-    // workgroups on every CU anyway (p.pair), a workgroup runs two query
-    // blocks one after the other, the heaviest and the lightest remaining
+    // Under causal masking, when pairing is on (p.pair: always with two
+    // groups, else when the launch keeps two workgroups on every CU anyway),
+    // a workgroup runs two query blocks one after the other, the heaviest and the lightest remaining
     // (n_qb-1-i, then i), so every workgroup streams the same number of key
     // tiles and the last query block does not set the kernel's time alone.
     // Otherwise one block per workgroup, heaviest first.
@@ -128,6 +146,11 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
     const int g = hq / p.group;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w4 = wave & 3;                  // 32-row slice of the query block
+    const int grp = NG == 2 ? wave >> 2 : 0;  // key half of the block
+    const int gtid = tid & (kMThreads - 1);   // thread index within the group
+    T* const vt = lds + grp * 2 * TILE;
+    T* const kt = vt + TILE;
     const int r = lane & 31, gl = lane >> 5;
     const int S = p.S;
     const int D = EXACT ? DP : p.D;
@@ -139,7 +162,7 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
     for (int sg = 0; sg < nseg; ++sg) {
         const int qb = sg == 0 ? qb0 : qb1;
         const int q0 = qb * kMRows;
-        const int qrow = q0 + wave * 32 + r;
+        const int qrow = q0 + w4 * 32 + r;
         const bool live = qrow < S;
 
         const int64_t qstride = int64_t(p.Hq) * D;
@@ -193,7 +216,7 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
                 // past the range), read as zeros without touching memory; no
                 // branch, so every load is in flight together (byte offsets
                 // fit 32 bits: S·Hkv·D·elt < 2^31 is checked on the host)
-                const int ch = tid + kMThreads * i, key = k0 + ch / CPR, col = 8 * (ch % CPR);
+                const int ch = gtid + kMThreads * i, key = k0 + ch / CPR, col = 8 * (ch % CPR);
                 const bool in_d = EXACT || col < D;
                 const int boff = in_d ? int((int64_t(key) * kvstride + col) * int64_t(sizeof(T))) : 0x7ffffff0;
                 vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, boff, 0, 0));
@@ -223,22 +246,33 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
                     }
             }
         };
-        if (ntile > 0) {
-            load_tile(0);
-            load_mask(0);
+        // this group's key tiles [tb, te); both groups run n_it iterations
+        // (the same barriers), an iteration past the group's range idles
+        const int t_mid = NG == 2 ? (ntile + 1) / 2 : ntile;
+        const int tb = grp == 0 ? 0 : t_mid;
+        const int te = grp == 0 ? t_mid : ntile;
+        const int n_it = t_mid;
+        if (tb < te) {
+            load_tile(tb);
+            load_mask(tb);
         }
-        for (int t = 0; t < ntile; ++t) {
+        for (int it = 0; it < n_it; ++it) {
+            const int t = tb + it;
+            const bool active = t < te;  // uniform over the group
             const int k0 = t * kMKeys;
             __syncthreads();  // every wavefront is done reading the previous K and V tiles
+            if (active) {
 #pragma unroll
-            for (int i = 0; i < NVL; ++i) {
-                const int ch = tid + kMThreads * i;
-                const int li = (ch / CPR) * ROWP + 8 * (ch % CPR);
-                *reinterpret_cast<u32x4*>(vt + li) = vreg[i];
-                *reinterpret_cast<u32x4*>(kt + li) = kreg[i];
+                for (int i = 0; i < NVL; ++i) {
+                    const int ch = gtid + kMThreads * i;
+                    const int li = (ch / CPR) * ROWP + 8 * (ch % CPR);
+                    *reinterpret_cast<u32x4*>(vt + li) = vreg[i];
+                    *reinterpret_cast<u32x4*>(kt + li) = kreg[i];
+                }
             }
             __syncthreads();  // the tiles are in place
-            if (t + 1 < ntile) load_tile(t + 1);
+            if (!active) continue;
+            if (t + 1 < te) load_tile(t + 1);
 
             // K operands from LDS: virtual row r of block blk is key 32·blk +
             // perm_row(r) of the tile, head dims 16c + 8gl .. +7
@@ -268,7 +302,7 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
                     mt = fmaxf(mt, sv);
                 }
             mt = fmaxf(mt, xor32(mt));
-            if (MASK && t + 1 < ntile) load_mask(t + 1);  // this tile's mask values are used
+            if (MASK && t + 1 < te) load_mask(t + 1);  // this tile's mask values are used
             const float m_new = fmaxf(m_run, mt);
             const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
             const float mu = m_new == -INFINITY ? 0.0f : m_new;
@@ -306,6 +340,37 @@ __global__ __launch_bounds__(kMThreads, DP > 128 ? 1 : 2) void masked_kernel(MPa
                         const op_t va = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
                         oacc[db] = Op<T>::mma(va, pop[blk][kc], oacc[db]);
                     }
+        }
+
+        // merge the two key halves: group 1 leaves (m, l, l_exact, Oᵀ) in LDS,
+        // group 0 combines m = max(m0, m1), O = O0·2^(m0-m) + O1·2^(m1-m),
+        // likewise the sums, and writes the block
+        if constexpr (NG == 2) {
+            __syncthreads();  // every tile read of this block is done
+            float* stash = reinterpret_cast<float*>(lds);
+            if (grp == 1) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int f = 0; f < 16; ++f) stash[((w4 * NDB + db) * 16 + f) * 64 + lane] = oacc[db][f];
+                s_ml[w4][0][lane] = m_run;
+                s_ml[w4][1][lane] = l_run;
+                s_ml[w4][2][lane] = l_ex;
+            }
+            __syncthreads();
+            if (grp == 1) continue;
+            const float m1 = s_ml[w4][0][lane];
+            const float mm = fmaxf(m_run, m1);
+            const float a0 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - mm);
+            const float a1 = mm == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int f = 0; f < 16; ++f)
+                    oacc[db][f] = oacc[db][f] * a0 + stash[((w4 * NDB + db) * 16 + f) * 64 + lane] * a1;
+            l_run = l_run * a0 + s_ml[w4][1][lane] * a1;
+            l_ex = l_ex * a0 + s_ml[w4][2][lane] * a1;
+            m_run = mm;
         }
 
         // O = Oᵀ / l (the sum of the rounded probabilities, over both lane halves),
@@ -353,14 +418,16 @@ int launch_m(const attn_detail::LaunchArgs& a) {
     mp.mask_h = a.mask_h;
     mp.sl2 = a.scale * 1.44269504088896340736f;
     mp.n_qb = int((a.S + kMRows - 1) / kMRows);
-    // pair heavy and light causal blocks only when the paired launch still
-    // has two workgroups for each of the 256 CUs: below that, two resident
-    // workgroups per CU (one wavefront of each per SIMD) hide more of the
-    // per-tile load latency than the balance gains
-    mp.pair = CAUSAL && int64_t((mp.n_qb + 1) / 2) * a.Hq * a.B >= 512 ? 1 : 0;
+    // Two-group workgroups (one per CU) always pair heavy and light causal
+    // blocks.  One-group workgroups pair them only when the paired launch
+    // still has two workgroups for each of the 256 CUs: below that, two
+    // resident workgroups per CU hide more of the per-tile load latency than
+    // the balance gains.
+    constexpr int NG = MGroups<DP>::value;
+    mp.pair = CAUSAL && (NG == 2 || int64_t((mp.n_qb + 1) / 2) * a.Hq * a.B >= 512) ? 1 : 0;
     const unsigned n_x = unsigned(mp.pair ? (mp.n_qb + 1) / 2 : mp.n_qb);
     hipLaunchKernelGGL((masked_kernel<T, DP, CAUSAL, MK, EXACT>), dim3(n_x, unsigned(a.Hq), unsigned(a.B)),
-                       dim3(kMThreads), 0, static_cast<hipStream_t>(a.stream), mp);
+                       dim3(kMThreads * NG), 0, static_cast<hipStream_t>(a.stream), mp);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return ATTN_OK;
     if (e == hipErrorNoBinaryForGpu || e == hipErrorInvalidDeviceFunction) return ATTN_ERR_DEVICE;
