@@ -100,7 +100,7 @@ __device__ __forceinline__ float xor32(float x) {
 // (element loads).  EXACT: D == DP, known at compile time (no head-dim
 // guards).
 //
-// Head dims up to 128 run two groups of four wavefronts per workgroup (NG =
+// Head dims up to 160 run two groups of four wavefronts per workgroup (NG =
 // 2): both groups take the same query block, group 0 its first half of the
 // key tiles and group 1 the second half, each with its own LDS tiles, and
 // the two partial softmax states (m, l, O) are merged through LDS at the end
@@ -109,7 +109,7 @@ __device__ __forceinline__ float xor32(float x) {
 // wavefront per SIMD).
 template <int DP>
 struct MGroups {
-    static constexpr int value = DP <= 128 ? 2 : 1;
+    static constexpr int value = DP <= 160 ? 2 : 1;
 };
 
 template <typename T, int DP, bool CAUSAL, int MK, bool EXACT>
