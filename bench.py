@@ -201,6 +201,9 @@ DECODE_SHAPES = {
     # 4096-token KV cache (64 query heads sharing 8 kv heads, D = 128, bf16)
     "llama2_70b_decode_b8": dict(B=8, Sq=1, Sk=4096, Hq=64, Hkv=8, D=128),
     "llama2_70b_decode_b2": dict(B=2, Sq=1, Sk=4096, Hq=64, Hkv=8, D=128),
+    # Llama-2-7B-shaped (MHA: one query head per kv head, so one real row
+    # per workgroup) decode step, 16 sequences
+    "llama2_7b_decode_b16": dict(B=16, Sq=1, Sk=4096, Hq=32, Hkv=32, D=128),
 }
 
 
