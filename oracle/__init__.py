@@ -62,5 +62,6 @@ from .varlen import (  # noqa: F401
 )
 from .masked import (  # noqa: F401
     mask_slice,
+    additive_from_bool,
     attention_masked,
 )

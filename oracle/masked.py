@@ -22,8 +22,9 @@ batch and heads (b' = b if Bm = B else 0, likewise h').
 
 Readings (listed in the design doc): the mask is additive (a value of -inf hides
 the key, 0 leaves it untouched, any finite value shifts the score), as the
-pages' float mask tensor and the "Scale → Mask → Softmax" order imply; it is
-applied after the scale; causal masking composes with it; a row whose every
+pages' float mask tensor and the "Scale → Mask → Softmax" order imply; a
+boolean mask (True: the key takes part, False: hidden) is the additive mask
+with 0 and -inf; it is applied after the scale; causal masking composes with it; a row whose every
 score is -inf has O = 0 and LSE = -inf; mask values are finite or -inf.
 """
 
@@ -38,12 +39,21 @@ def mask_slice(mask, b, h):
     return mask[b if bm > 1 else 0, h if hm > 1 else 0]
 
 
+def additive_from_bool(mask):
+    """A boolean mask (True: the key takes part) as the additive mask it
+    stands for: 0 where True, -inf where False."""
+    mask = np.asarray(mask)
+    return np.where(mask.astype(bool), 0.0, -np.inf)
+
+
 def attention_masked(q, k, v, mask, *, causal=False, scale=None):
-    """O (B, S, Hq, D) and LSE (B, Hq, S) under an additive mask, float64."""
+    """O (B, S, Hq, D) and LSE (B, Hq, S) under an additive mask (or a
+    boolean one, read through additive_from_bool), float64."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    mask = np.asarray(mask, dtype=np.float64)
+    mask = np.asarray(mask)
+    mask = additive_from_bool(mask) if mask.dtype == bool else mask.astype(np.float64)
     b_n, s, hq, d = q.shape
     hkv = k.shape[2]
     if k.shape[:2] != (b_n, s) or v.shape != k.shape or k.shape[3] != d:

@@ -7,7 +7,9 @@ for the causal flag; -inf past L_b standing in for key padding), torch's CPU
 scaled_dot_product_attention in float64 with a float (additive) mask under
 every broadcast shape (an independent library routine), the shift
 invariance of the softmax (a per-row constant in the mask moves only LSE, by
-exactly that constant), and closed forms for fully masked rows.
+exactly that constant), closed forms for fully masked rows, and a boolean
+mask against both the hand-built additive one and torch's SDPA given the same
+boolean mask.
 """
 
 import math
@@ -127,6 +129,32 @@ def pin_masked_fully_masked_rows(orc):
     _close(l[0][:, keep], pl[0][:, keep], 1e-12, "other rows LSE")
 
 
+def pin_masked_bool_mask(orc):
+    """A boolean mask (True: the key takes part) equals the additive mask of
+    zeros and -inf built by hand, and torch's CPU SDPA given the same boolean
+    mask (its own convention: True takes part) in float64."""
+    import torch
+
+    rng = np.random.default_rng(37)
+    b, s, hq, hkv, d = 2, 9, 4, 2, 8
+    q, k, v = _qkv(rng, b, s, hq, hkv, d)
+    bm = rng.random((b, 1, s, s)) < 0.7
+    bm[..., 0] = True  # every row keeps a key
+    add = np.zeros(bm.shape)
+    add[~bm] = -np.inf
+    for causal in (False, True):
+        o, l = orc.attention_masked(q, k, v, bm, causal=causal)
+        ao, al = orc.attention_masked(q, k, v, add, causal=causal)
+        _close(o, ao, 0.0, f"O bool vs additive causal={causal}")
+        _close(l, al, 0.0, f"LSE bool vs additive causal={causal}")
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(hq // hkv, dim=1)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(hq // hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(bm))
+    o, _ = orc.attention_masked(q, k, v, bm)
+    _close(o, ref.permute(0, 2, 1, 3).numpy(), 1e-12, "O vs torch bool mask")
+
+
 ALL_PINS = [
     pin_masked_zero_mask_is_plain,
     pin_masked_triangle_is_causal,
@@ -134,4 +162,5 @@ ALL_PINS = [
     pin_masked_torch_sdpa,
     pin_masked_row_shift,
     pin_masked_fully_masked_rows,
+    pin_masked_bool_mask,
 ]

@@ -242,6 +242,8 @@ MASKED_MUTANTS = {
                         "lse[b, h, :] = np.where(has_key, np.log(safe), -np.inf)"),
     "gqa_interleaved": ("g = (h * hkv) // hq", "g = h % hkv"),
     "default_scale_1_over_d": ("scale = 1.0 / math.sqrt(d)", "scale = 1.0 / d"),
+    "bool_inverted": ("return np.where(mask.astype(bool), 0.0, -np.inf)",
+                      "return np.where(mask.astype(bool), -np.inf, 0.0)"),
 }
 
 
