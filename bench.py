@@ -16,7 +16,7 @@ a bounded sample of heads of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--all] [--sweep] [--rope] [--decode] [--varlen] [--masked]
-                    [--general-d]
+                    [--general-d] [--write-traffic PROF_DIR]
                     [--copy-calibration]
 """
 
@@ -161,6 +161,39 @@ def copy_calibration(nbytes=1 << 29, reps=3):
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
                       "kernel_source_sha": kernel_source_sha()}), flush=True)
+
+
+def write_traffic(prof_dir, name=DEFAULT_WORKLOAD):
+    """Write profiles/traffic_<name>.json from four rocprofv3 --pmc runs under
+    prof_dir (fetch_c2, write_c2: the benchmark; fetch_copy, write_copy: the
+    512 MiB copy calibration), each holding p_counter_collection.csv: the
+    attention kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the counter reads for the copy of known size."""
+    import csv
+    import statistics
+
+    def values(sub, kernel):
+        path = os.path.join(prof_dir, sub, "p_counter_collection.csv")
+        return [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]]
+
+    nbytes_kib = (1 << 29) / 1024.0
+    fetch, write = values("fetch_c2", "attn_fwd_kernel"), values("write_c2", "attn_fwd_kernel")
+    fscale = nbytes_kib / statistics.median(values("fetch_copy", "copyBuffer"))
+    wscale = nbytes_kib / statistics.median(values("write_copy", "copyBuffer"))
+    fk, wk = statistics.mean(fetch), statistics.mean(write)
+    cmd = "rocprofv3 --pmc {c} --output-format csv -d {d}/{sub} -o p -- python3 bench.py {args}"
+    out = {"workload": name, "kernel_source_sha": kernel_source_sha(),
+           "fetch_size_kib_per_dispatch": fk, "write_size_kib_per_dispatch": wk,
+           "fetch_scale": fscale, "write_scale": wscale,
+           "traffic_bytes_per_launch": (fk * fscale + wk * wscale) * 1024.0,
+           "commands": [cmd.format(c=c, d=prof_dir, sub=sub, args=args) for c, sub, args in (
+               ("FETCH_SIZE", "fetch_c2", "--steps 5 --warmup 2 --no-cpu-baseline"),
+               ("WRITE_SIZE", "write_c2", "--steps 5 --warmup 2 --no-cpu-baseline"),
+               ("FETCH_SIZE", "fetch_copy", "--copy-calibration"),
+               ("WRITE_SIZE", "write_copy", "--copy-calibration"))]}
+    with open(os.path.join(ROOT, "profiles", f"traffic_{name}.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -415,6 +448,9 @@ def main():
     ap.add_argument("--all", action="store_true", help="one line per workload (no CPU leg)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of a replayed HIP graph of the K steps")
+    ap.add_argument("--write-traffic", metavar="PROF_DIR",
+                    help="write profiles/traffic_<workload>.json from the four rocprofv3 --pmc runs under PROF_DIR "
+                         "(no GPU needed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
     ap.add_argument("--decode", action="store_true",
@@ -435,6 +471,9 @@ def main():
     warmup_s = 0.5 if args.warmup is None else 0.0
     if args.warmup is None:
         args.warmup = 20
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)

@@ -70,6 +70,12 @@ typedef enum {
     ATTN_MASK_KEY_PADDING = 1  /* batch b sees keys j < pad_lens[b] only       */
 } attn_mask_kind_t;
 
+/* Element type of attn_fwd_masked's mask tensor. */
+typedef enum {
+    ATTN_MASK_ADDITIVE = 0,  /* q's dtype, added to the scaled scores (-inf hides) */
+    ATTN_MASK_BOOL = 1       /* one byte per entry: nonzero = the key takes part */
+} attn_mask_type_t;
+
 /* Tensor descriptor: a contiguous (B, S, H, D) device buffer. */
 typedef struct {
     void*   data;   /* device pointer, 16-byte aligned                        */
@@ -174,14 +180,16 @@ int attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k, const attn_t
  *
  *   S_ij = (Q_i · K_j) · scale + M[b', h', i, j]
  *
- * where M is (mask_B, mask_H, S, S), contiguous, row-major, in q's dtype,
- * broadcast over batch (mask_B == 1: b' = 0; mask_B == B: b' = b) and query
- * heads (mask_H == 1 or Hq).  -inf hides a key; a row whose every score is
- * -inf is written as zeros with LSE -inf.  causal (0/1) composes with the
- * mask (j > i is hidden as well).
+ * where M is (mask_B, mask_H, S, S), contiguous, row-major, broadcast over
+ * batch (mask_B == 1: b' = 0; mask_B == B: b' = b) and query heads (mask_H
+ * == 1 or Hq).  -inf hides a key; a row whose every score is -inf is written
+ * as zeros with LSE -inf.  causal (0/1) composes with the mask (j > i is
+ * hidden as well).
  *
- *   mask        device pointer, 16-byte aligned (ATTN_ERR_ALIGN), values
- *               finite or -inf.
+ *   mask        device pointer, 16-byte aligned (ATTN_ERR_ALIGN).
+ *   mask_type   ATTN_MASK_ADDITIVE: M in q's dtype, values finite or -inf;
+ *               ATTN_MASK_BOOL: one byte per entry, nonzero = the key takes
+ *               part (M = 0), zero = hidden (M = -inf).  Else ATTN_ERR_MASK.
  *   mask_B      1 or q->B; mask_H  1 or n_q_heads (else ATTN_ERR_MASK).
  *   q, k, v, scale, causal, n_q_heads, n_kv_heads, out, lse, stream: as for
  *               attn_fwd (no key-padding argument: a mask expresses it).
@@ -190,7 +198,7 @@ int attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k, const attn_t
  * multiple of 16 in [16, 256], B <= 65535.  One launch; all checks precede it.
  */
 int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
-                    const void* mask, int64_t mask_B, int64_t mask_H, float scale, int causal,
+                    const void* mask, int mask_type, int64_t mask_B, int64_t mask_H, float scale, int causal,
                     int n_q_heads, int n_kv_heads, const attn_tensor_t* out, float* lse, void* stream);
 
 /*

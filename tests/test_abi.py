@@ -284,8 +284,8 @@ def test_varlen_empty_returns_ok_without_launch(lib):
 # --------------------------------------------------------------------------
 # attn_fwd_masked: additive mask tensor, host only
 # --------------------------------------------------------------------------
-def call_mask(lib, q, k, v, out, mask=FAKE + 0x300000, mb=1, mh=1, causal=0, lse=None):
-    return lib.attn_fwd_masked(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), mask, ctypes.c_int64(mb),
+def call_mask(lib, q, k, v, out, mask=FAKE + 0x300000, mb=1, mh=1, causal=0, lse=None, mtype=0):
+    return lib.attn_fwd_masked(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), mask, mtype, ctypes.c_int64(mb),
                                ctypes.c_int64(mh), ctypes.c_float(0.0), causal, q.H, k.H, ctypes.byref(out), lse,
                                None)
 
@@ -296,6 +296,8 @@ def test_masked_checks(lib):
     assert call_mask(lib, T(B=2, H=4, **f32), T(B=2, H=2, **f32), T(B=2, H=2, **f32),
                      T(B=2, H=4, **f32)) == A.ATTN_ERR_UNSUPPORTED            # 16-bit types only
     assert call_mask(lib, q, k, v, o, mb=3) == A.ATTN_ERR_MASK                # batch dim neither 1 nor B
+    assert call_mask(lib, q, k, v, o, mtype=2) == A.ATTN_ERR_MASK             # unknown mask type
+    assert call_mask(lib, q, k, v, o, mtype=A.ATTN_MASK_BOOL, mask=FAKE + 8) == A.ATTN_ERR_ALIGN
     assert call_mask(lib, q, k, v, o, mh=2) == A.ATTN_ERR_MASK                # head dim neither 1 nor Hq
     assert call_mask(lib, q, k, v, o, mask=None) == A.ATTN_ERR_NULL
     assert call_mask(lib, q, k, v, o, mask=FAKE + 8) == A.ATTN_ERR_ALIGN

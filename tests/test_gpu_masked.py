@@ -151,3 +151,46 @@ def test_masked_causal_paired_blocks(B, S, Hq, Hkv, D, dtype, mshape):
     shape = (1, 1, S, S) if mshape == "11" else (B, 1, S, S)
     o, l, ro, rl = _run(15 + B, B, S, Hq, Hkv, D, dtype, shape, True)
     assert_parity(o, ro, dtype, lse=l, lse_ref=rl, what=f"paired B{B} S{S}")
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,dtype,causal,si", [
+    (2, 200, 4, 2, 128, "bf16", False, 0),
+    (2, 200, 4, 2, 128, "bf16", True, 1),
+    (2, 203, 4, 4, 64, "fp16", False, 2),   # S % 8 != 0: byte loads
+    (1, 129, 2, 1, 64, "bf16", True, 3),
+    (2, 96, 4, 2, 80, "fp16", True, 1),     # general head dim
+])
+def test_masked_bool(B, S, Hq, Hkv, D, dtype, causal, si):
+    """A torch.bool mask (True: the key takes part), every broadcast shape,
+    against the oracle reading the same boolean mask; rows with no True key
+    give zeros and LSE -inf."""
+    rng = np.random.default_rng(50 + si)
+    q = rng.standard_normal((B, S, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((B, S, Hkv, D)).astype(np.float32)
+    shape = SHAPES(B, Hq, S)[si]
+    bm = rng.random(shape) < 0.6
+    bm[..., 5, :] = False  # a row with no visible key
+    qd, qn = prep(q, dtype)
+    kd, kn = prep(k, dtype)
+    vd, vn = prep(v, dtype)
+    md = torch.from_numpy(bm).cuda()
+    print(f"masked bool case B{B} S{S} H{Hq}/{Hkv} D{D} {dtype} mask={shape} causal={causal}", flush=True)
+    out, l = A.masked_attention(qd, kd, vd, md, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_masked(qn, kn, vn, bm, causal=causal)
+    assert_parity(to_np(out), ro, dtype, lse=l.cpu().numpy(), lse_ref=rl, what=f"bool mask {shape}")
+
+
+def test_masked_bool_equals_additive():
+    """The same mask as bool and as additive 0 / -inf gives identical outputs."""
+    rng = np.random.default_rng(60)
+    B, S, Hq, Hkv, D = 1, 256, 4, 2, 128
+    q, k, v = (prep(rng.standard_normal((B, S, h, D)).astype(np.float32), "bf16")[0] for h in (Hq, Hkv, Hkv))
+    bm = rng.random((1, Hq, S, S)) < 0.5
+    add = torch.from_numpy(np.where(bm, 0.0, -np.inf).astype(np.float32)).to(torch.bfloat16).cuda()
+    print("masked bool vs additive", flush=True)
+    ob, lb = A.masked_attention(q, k, v, torch.from_numpy(bm).cuda(), causal=True, return_lse=True)
+    oa, la = A.masked_attention(q, k, v, add, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ob, oa) and torch.equal(lb, la)

@@ -27,6 +27,8 @@ ATTN_ERR_LAUNCH = -8
 ATTN_ERR_DEVICE = -9
 ATTN_ERR_ALIAS = -10
 ATTN_ERR_WORKSPACE = -11
+ATTN_MASK_ADDITIVE = 0
+ATTN_MASK_BOOL = 1
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_masked", "attn_fwd_rope", "attn_fwd_decode",
                     "attn_decode_workspace_bytes", "attn_strerror", "attn_version")
@@ -65,7 +67,7 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd_varlen.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_fwd_varlen.restype = ctypes.c_int
-    lib.attn_fwd_masked.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+    lib.attn_fwd_masked.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_fwd_masked.restype = ctypes.c_int
     lib.attn_fwd_rope.argtypes = [P, P, P, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_int,
@@ -277,14 +279,19 @@ def varlen_attention(q, k, v, cu_seqlens, max_seqlen, *, causal=False, scale=Non
 
 def attn_fwd_masked(q, k, v, mask, scale, causal, n_q_heads, n_kv_heads, out, lse, stream=None):
     """``attn_fwd_masked`` with torch tensors: q, k, v, out as for attn_fwd
-    (bf16/fp16); mask: contiguous (1 or B, 1 or Hq, S, S) device tensor of
-    q's dtype, added to the scaled scores (-inf hides a key)."""
+    (bf16/fp16); mask: contiguous (1 or B, 1 or Hq, S, S) device tensor,
+    either of q's dtype (added to the scaled scores, -inf hides a key) or
+    torch.bool (True: the key takes part)."""
     import torch
     lib = load_library()
     _, lse_ptr = _common_ptrs(q, k, v, out, None, lse, n_q_heads)
     if not mask.is_cuda or not mask.is_contiguous() or mask.dim() != 4:
         raise ValueError("mask must be a contiguous 4-D device tensor (1|B, 1|Hq, S, S)")
-    if mask.dtype != q.dtype:
+    if mask.dtype == torch.bool:
+        mask_type = ATTN_MASK_BOOL
+    elif mask.dtype == q.dtype:
+        mask_type = ATTN_MASK_ADDITIVE
+    else:
         raise AttnArgumentError(ATTN_ERR_DTYPE)
     if tuple(mask.shape[2:]) != (q.shape[1], q.shape[1]):
         raise AttnArgumentError(ATTN_ERR_MASK)
@@ -292,7 +299,7 @@ def attn_fwd_masked(q, k, v, mask, scale, causal, n_q_heads, n_kv_heads, out, ls
         stream = torch.cuda.current_stream(q.device)
     dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
     code = lib.attn_fwd_masked(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), ctypes.c_void_p(mask.data_ptr()),
-                               int(mask.shape[0]), int(mask.shape[1]),
+                               int(mask_type), int(mask.shape[0]), int(mask.shape[1]),
                                ctypes.c_float(0.0 if scale is None else float(scale)), int(bool(causal)),
                                int(n_q_heads), int(n_kv_heads), ctypes.byref(do), lse_ptr,
                                ctypes.c_void_p(stream.cuda_stream))

@@ -163,7 +163,8 @@ extern "C" int attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k, c
 // V, mask, scale); [ATB-guide] §8.2 passes the mask as one more FP16 input):
 // a kernel of its own that reads the mask block of every tile.
 extern "C" int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
-                               const void* mask, int64_t mask_B, int64_t mask_H, float scale, int causal,
+                               const void* mask, int mask_type, int64_t mask_B, int64_t mask_H, float scale,
+                               int causal,
                                int n_q_heads, int n_kv_heads, const attn_tensor_t* out, float* lse,
                                void* stream) {
     attn_detail::LaunchArgs a;
@@ -172,6 +173,7 @@ extern "C" int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, c
                            stream, a, empty, true);
     if (rc != ATTN_OK) return rc;
     if (q->dtype == ATTN_F32) return ATTN_ERR_UNSUPPORTED;  // 16-bit types only
+    if (mask_type != ATTN_MASK_ADDITIVE && mask_type != ATTN_MASK_BOOL) return ATTN_ERR_MASK;
     if (mask_B != 1 && mask_B != q->B) return ATTN_ERR_MASK;
     if (mask_H != 1 && mask_H != n_q_heads) return ATTN_ERR_MASK;
     if (empty) return ATTN_OK;
@@ -181,6 +183,7 @@ extern "C" int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, c
     a.mask = mask;
     a.mask_b = mask_B != 1 ? 1 : 0;
     a.mask_h = mask_H != 1 ? 1 : 0;
+    a.mask_bool = mask_type == ATTN_MASK_BOOL ? 1 : 0;
     return attn_detail::launch_masked(a);
 }
 

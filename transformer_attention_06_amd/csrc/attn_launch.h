@@ -36,6 +36,7 @@ struct LaunchArgs {
     // when the mask has a batch dimension of B / a head dimension of Hq
     const void* mask = nullptr;
     int mask_b = 0, mask_h = 0;
+    int mask_bool = 0;  // 1: one byte per entry, nonzero = the key takes part
 };
 
 // Enqueue the kernel; returns ATTN_OK or ATTN_ERR_LAUNCH / ATTN_ERR_DEVICE.

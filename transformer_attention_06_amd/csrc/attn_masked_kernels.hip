@@ -97,7 +97,9 @@ __device__ __forceinline__ float xor32(float x) {
 // and head-dim chunks at or past it are read as zeros and not written.
 // MK: 0 no mask tensor; 1 an additive mask tensor whose rows are 16-byte
 // aligned (S a multiple of 8: 16-byte loads); 2 the same with unaligned rows
-// (element loads).  EXACT: D == DP, known at compile time (no head-dim
+// (element loads); 3 a boolean mask (one byte per entry, nonzero: the key
+// takes part) with 8-byte aligned rows (8-byte loads); 4 the same unaligned
+// (byte loads).  EXACT: D == DP, known at compile time (no head-dim
 // guards).
 //
 // Head dims up to 160 run two groups of four wavefronts per workgroup (NG =
@@ -116,6 +118,7 @@ template <typename T, int DP, bool CAUSAL, int MK, bool EXACT>
 __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kernel(MParams p) {
     using op_t = typename Op<T>::op_t;
     constexpr bool MASK = MK != 0;
+    constexpr bool BMASK = MK >= 3;  // boolean mask
     constexpr int NG = MGroups<DP>::value;
     constexpr int NC = DP / 16;                    // MFMA steps along the head dim for Sᵀ
     constexpr int NDB = DP / 32;                   // 32-dim blocks of Oᵀ
@@ -170,7 +173,9 @@ __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kern
         const T* kb = static_cast<const T*>(p.k) + int64_t(b) * S * kvstride + int64_t(g) * D;
         const T* vb = static_cast<const T*>(p.v) + int64_t(b) * S * kvstride + int64_t(g) * D;
         const int64_t plane = int64_t(p.mask_b ? b : 0) * (p.mask_h ? p.Hq : 1) + (p.mask_h ? hq : 0);
-        const T* mrow = MASK ? static_cast<const T*>(p.mask) + (plane * S + (live ? qrow : 0)) * int64_t(S) : nullptr;
+        const int64_t mrow_off = (plane * S + (live ? qrow : 0)) * int64_t(S);
+        const T* mrow = MASK && !BMASK ? static_cast<const T*>(p.mask) + mrow_off : nullptr;
+        const uint8_t* mrow8 = BMASK ? static_cast<const uint8_t*>(p.mask) + mrow_off : nullptr;
 
         // Q operand: the lane's row, head dims 16c + 8gl .. +7
         op_t qop[NC];
@@ -201,7 +206,8 @@ __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kern
         // zeros.  Tile t+1's mask values are loaded as soon as tile t's
         // scores have taken theirs (one register set).
         u32x4 vreg[NVL], kreg[NVL];
-        op_t mnext[2][2];
+        op_t mnext[2][2];     // additive mask values of the next tile
+        uint64_t bnext[2][2];  // boolean mask bytes of the next tile
         const int nrec = key_lim > 0 ? int((int64_t(key_lim) * kvstride - int64_t(g) * D) * int64_t(sizeof(T))) : 0;
         const __amdgpu_buffer_rsrc_t krs =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(kb), 0, nrec, 0x00020000);
@@ -239,9 +245,17 @@ __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kern
                         const int key0 = k0 + 32 * blk + 16 * h + 8 * gl;
                         if constexpr (MK == 1) {
                             mnext[blk][h] = *reinterpret_cast<const op_t*>(mrow + (key0 + 8 <= S ? key0 : S - 8));
-                        } else {
+                        } else if constexpr (MK == 2) {
 #pragma unroll
                             for (int e = 0; e < 8; ++e) mnext[blk][h][e] = mrow[key0 + e < S ? key0 + e : S - 1];
+                        } else if constexpr (MK == 3) {
+                            bnext[blk][h] = *reinterpret_cast<const uint64_t*>(mrow8 + (key0 + 8 <= S ? key0 : S - 8));
+                        } else {
+                            uint64_t w = 0;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                w |= uint64_t(mrow8[key0 + e < S ? key0 + e : S - 1]) << (8 * e);
+                            bnext[blk][h] = w;
                         }
                     }
             }
@@ -295,8 +309,10 @@ __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kern
                 for (int f = 0; f < 16; ++f) {
                     const int key = k0 + 32 * blk + acc_pos(f, gl);
                     float sv = sacc[blk][f] * p.sl2;
-                    if constexpr (MASK) sv = fmaf(float(mnext[blk][(f >> 3) & 1][f & 7]), 1.44269504088896340736f, sv);
-                    const bool ok = key < key_lim && (!CAUSAL || key <= qrow);
+                    if constexpr (MASK && !BMASK)
+                        sv = fmaf(float(mnext[blk][(f >> 3) & 1][f & 7]), 1.44269504088896340736f, sv);
+                    bool ok = key < key_lim && (!CAUSAL || key <= qrow);
+                    if constexpr (BMASK) ok = ok && ((bnext[blk][(f >> 3) & 1] >> (8 * (f & 7))) & 0xff) != 0;
                     sv = ok ? sv : -INFINITY;
                     sacc[blk][f] = sv;
                     mt = fmaxf(mt, sv);
@@ -444,6 +460,7 @@ int launch_mc(const attn_detail::LaunchArgs& a) {
 template <typename T, int DP, bool MASK>
 int launch_mk(const attn_detail::LaunchArgs& a) {
     if (!MASK) return launch_mc<T, DP, 0>(a);
+    if (a.mask_bool) return a.S % 8 == 0 ? launch_mc<T, DP, 3>(a) : launch_mc<T, DP, 4>(a);
     return a.S % 8 == 0 ? launch_mc<T, DP, 1>(a) : launch_mc<T, DP, 2>(a);
 }
 
