@@ -129,7 +129,10 @@ __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kern
     constexpr int TILE = kMKeys * ROWP;            // elements per K (or V) tile
     // per group: V tile, then K tile; after a block the region holds group
     // 1's partial output for the merge
-    __shared__ __attribute__((aligned(16))) T lds[NG * 2 * TILE];
+    // two K/V buffers per group where LDS holds them (one barrier per tile),
+    // else one (two barriers per tile)
+    constexpr int NBUF = (NG * 2 * 2 * TILE * int(sizeof(T)) + 3072 <= 160 * 1024) ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) T lds[NG * NBUF * 2 * TILE];
     __shared__ float s_ml[4][3][64];
     static_assert(NG == 1 || 4 * (DP / 32) * 16 * 64 * 4 <= int(sizeof(lds)), "merge stash fits the tiles");
 
@@ -152,8 +155,7 @@ __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kern
     const int w4 = wave & 3;                  // 32-row slice of the query block
     const int grp = NG == 2 ? wave >> 2 : 0;  // key half of the block
     const int gtid = tid & (kMThreads - 1);   // thread index within the group
-    T* const vt = lds + grp * 2 * TILE;
-    T* const kt = vt + TILE;
+    T* const gbuf = lds + grp * NBUF * 2 * TILE;  // this group's buffers: V tile, then K tile, per buffer
     const int r = lane & 31, gl = lane >> 5;
     const int S = p.S;
     const int D = EXACT ? DP : p.D;
@@ -266,27 +268,51 @@ __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kern
         const int tb = grp == 0 ? 0 : t_mid;
         const int te = grp == 0 ? t_mid : ntile;
         const int n_it = t_mid;
+        // the staged registers (one tile's V and K rows) into LDS buffer buf
+        auto write_tile = [&](int buf) __attribute__((always_inline)) {
+            T* const vw = gbuf + buf * 2 * TILE;
+#pragma unroll
+            for (int i = 0; i < NVL; ++i) {
+                const int ch = gtid + kMThreads * i;
+                const int li = (ch / CPR) * ROWP + 8 * (ch % CPR);
+                *reinterpret_cast<u32x4*>(vw + li) = vreg[i];
+                *reinterpret_cast<u32x4*>(vw + TILE + li) = kreg[i];
+            }
+        };
         if (tb < te) {
             load_tile(tb);
             load_mask(tb);
+        }
+        if constexpr (NBUF == 2) {
+            // tile tb into buffer 0 and tile tb+1's loads in flight; the
+            // first barrier also covers the previous block's reads (and the
+            // merge stash)
+            __syncthreads();
+            if (tb < te) {
+                write_tile(0);
+                if (tb + 1 < te) load_tile(tb + 1);
+            }
+            __syncthreads();
         }
         for (int it = 0; it < n_it; ++it) {
             const int t = tb + it;
             const bool active = t < te;  // uniform over the group
             const int k0 = t * kMKeys;
-            __syncthreads();  // every wavefront is done reading the previous K and V tiles
-            if (active) {
-#pragma unroll
-                for (int i = 0; i < NVL; ++i) {
-                    const int ch = gtid + kMThreads * i;
-                    const int li = (ch / CPR) * ROWP + 8 * (ch % CPR);
-                    *reinterpret_cast<u32x4*>(vt + li) = vreg[i];
-                    *reinterpret_cast<u32x4*>(kt + li) = kreg[i];
+            const int cur = NBUF == 2 ? (it & 1) : 0;
+            if constexpr (NBUF == 1) {
+                __syncthreads();  // every wavefront is done reading the previous K and V tiles
+                if (active) write_tile(0);
+                __syncthreads();  // the tiles are in place
+                if (!active) continue;
+                if (t + 1 < te) load_tile(t + 1);
+            } else {
+                if (!active) {  // idle iteration: the same single barrier
+                    __syncthreads();
+                    continue;
                 }
             }
-            __syncthreads();  // the tiles are in place
-            if (!active) continue;
-            if (t + 1 < te) load_tile(t + 1);
+            const T* const vt = gbuf + cur * 2 * TILE;
+            const T* const kt = vt + TILE;
 
             // K operands from LDS: virtual row r of block blk is key 32·blk +
             // perm_row(r) of the tile, head dims 16c + 8gl .. +7
@@ -356,6 +382,16 @@ __global__ __launch_bounds__(kMThreads * MGroups<DP>::value, 1) void masked_kern
                         const op_t va = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
                         oacc[db] = Op<T>::mma(va, pop[blk][kc], oacc[db]);
                     }
+            if constexpr (NBUF == 2) {
+                // tile t+1 (its loads landed during this tile) into the other
+                // buffer, tile t+2's loads in flight; one barrier publishes it
+                // and retires this tile's reads of the current buffer
+                if (t + 1 < te) {
+                    write_tile(cur ^ 1);
+                    if (t + 2 < te) load_tile(t + 2);
+                }
+                __syncthreads();
+            }
         }
 
         // merge the two key halves: group 1 leaves (m, l, l_exact, Oᵀ) in LDS,
