@@ -5,8 +5,10 @@ Cases cover every broadcast shape of the mask ((1|B, 1|Hq, S, S)), sequence
 lengths at and around the 64-key tile and 128-row block (including S not a
 multiple of 8, where mask rows are not 16-byte aligned), finite shifts and
 -inf holes, fully masked rows, the causal flag composed with a mask, GQA,
-bf16 and fp16, D = 64 and 128, and a Llama-2-7B-shaped layer (S = 2048,
-D = 128, bf16) with a causal mask given as a tensor.
+bf16 and fp16, D = 64 and 128, a Llama-2-7B-shaped layer (S = 2048,
+D = 128, bf16) with a causal mask given as a tensor, and boolean masks
+(torch.bool, True: the key takes part) including their equality with the
+additive 0 / -inf form.
 """
 
 import numpy as np
