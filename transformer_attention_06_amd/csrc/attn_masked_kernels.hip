@@ -1,26 +1,33 @@
-// attn_masked_kernels.hip — fused attention forward with an explicit additive
-// mask tensor (gfx950).
+// attn_masked_kernels.hip — fused attention forward with an explicit mask
+// tensor, and the general-head-dim attention (gfx950).
 //
 // "CANN-ATB图优化-昇腾NPU怎么把PyTorch计算图改造成融合算子" Pattern 2 fuses
 // Q·Kᵀ → Scale → Mask → Softmax → ·V into FlashAttention(Q, K, V, mask,
 // scale), and the ATB engineering guide (hwcomputing.csdn.net/
 // 6a59a88310ee7a33f28e5ce9) §8.2 hands the mask to the operator as one more
-// FP16 input tensor.  Here the mask M (1 or B, 1 or Hq, S, S), in the input
-// type, is added to the scaled scores; -inf hides a key.
+// FP16 input tensor.  Here the mask M (1 or B, 1 or Hq, S, S) is added to the
+// scaled scores, in the input type (-inf hides a key), or given as one byte
+// per entry (nonzero: the key takes part).  The same kernel without a mask
+// serves head dims other than 64 and 128 ("CANN-ops-transformer和ATB…" gates
+// head_dim on multiples of 16), the head dim padded to a multiple of 32 in
+// registers and LDS only.
 //
-// One workgroup (4 wavefronts) owns one (batch, query head, 128-row query
-// block); each wavefront owns 32 query rows, one per lane, in the transposed
-// MFMA form of the prefill kernel: Sᵀ = K·Qᵀ and Oᵀ += Vᵀ·Pᵀ on 32x32x16
-// MFMA.  Per 64-key tile every lane loads the 32 mask values of its row that
-// its score registers hold (four 16-byte loads: the permuted K order makes
-// them four runs of 8 consecutive keys); the K and V tiles are staged once
-// per workgroup in LDS (V read back with the transposing LDS read), and the
-// next tile's K, V and mask loads are in flight while the current tile is
+// A group of 4 wavefronts owns one (batch, query head, 128-row query block);
+// each wavefront owns 32 query rows, one per lane, in the transposed MFMA
+// form of the prefill kernel: Sᵀ = K·Qᵀ and Oᵀ += Vᵀ·Pᵀ on 32x32x16 MFMA.
+// Up to head dim 160 a workgroup holds two such groups splitting the block's
+// key tiles (merged through LDS at the end), and under causal masking a
+// workgroup runs the heaviest and the lightest block in turn.  Per 64-key
+// tile every lane loads the 32 mask values of its row that its score
+// registers hold (four runs of 8 consecutive keys, thanks to the permuted K
+// order); the K and V tiles are staged per group in LDS (V read back with the
+// transposing LDS read), double-buffered where LDS allows, and the next
+// tile's K, V and mask loads are in flight while the current tile is
 // computed ("ops-transformer：Transformer算子融合与推理加速实战" §2.3: prefetch
 // the next block during the current one).  The online softmax keeps fp32
 // running max and sums per row (§3.2) and rescales the output accumulator
-// whenever the max rises.  Unlike the unmasked kernel the MFMAs and the
-// softmax are not interleaved by hand.
+// whenever the max rises.  Unlike the tuned D = 64/128 kernel the MFMAs and
+// the softmax are not interleaved by hand.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
