@@ -1,7 +1,9 @@
 // attn_fwd_kernels.hip — fused attention forward for gfx950 (MI355X).
 //
-// One workgroup (4 wavefronts of 64 lanes) owns one (batch, query head,
-// 128-row query block); each wavefront owns 32 query rows.  K/V tiles of BN
+// A group of 4 wavefronts of 64 lanes owns one (batch, query head, 128-row
+// query block); each wavefront owns 32 query rows.  A workgroup is one group,
+// or two under causal masking with 16-bit inputs (a heavy and a light block
+// of one head, see the work decomposition below).  K/V tiles of BN
 // keys stream through double-buffered LDS; the score tile, the online-softmax
 // state and the output accumulator never leave registers, so the S×S score
 // matrix never reaches device memory ("ops-transformer：Transformer算子融合与
@@ -242,19 +244,22 @@ __device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t lds_byte, ui
                  : "memory");
 }
 
-// Wavefront groups per workgroup: two for the 16-bit types (eight wavefronts,
-// two per SIMD), one for fp32 (whose registers do not fit twice per SIMD).
-template <typename T>
+// Wavefront groups per workgroup: two for the 16-bit types under causal
+// masking (eight wavefronts, two per SIMD, a heavy and a light query block
+// in one workgroup), otherwise one: without causal masking every block of a
+// sequence costs the same, so independent 4-wave workgroups (two per CU)
+// need no pairing and no shared barrier; fp32 registers do not fit twice per
+// SIMD.
+template <typename T, bool CAUSAL>
 struct Groups {
-    static constexpr int value = sizeof(T) == 2 ? 2 : 1;
+    static constexpr int value = sizeof(T) == 2 && CAUSAL ? 2 : 1;
 };
 
-// Work of one workgroup: one (batch, query head, 128-row query block); four
-// wavefronts of 32 rows each.  Two workgroups share a CU (two wavefronts per
-// SIMD), so the stalls of one wavefront's stream are filled by the other's.
-// Under causal masking the first half of the launch takes the blocks
-// heaviest first and the second half lightest first, so the workgroups that
-// end up sharing a CU even out.
+// Work of one group: one (batch, query head, 128-row query block); four
+// wavefronts of 32 rows each.  Two groups share a CU (two wavefronts per
+// SIMD), so the stalls of one wavefront's stream are filled by the other's:
+// two one-group workgroups, or one workgroup of two groups pairing a causal
+// heavy and light block.
 //
 // Each wavefront software-pipelines its own tile loop.  Step j (key tile j)
 // is one fixed instruction stream of two parts:
@@ -268,7 +273,7 @@ struct Groups {
 // (one 1 KiB direct load per wavefront every few MFMAs) and ends with a wait
 // for those loads and one workgroup barrier.
 template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE>
-__global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn_fwd_kernel(KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
     constexpr int KPL = E::KPL;
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
     constexpr int NKC = BN / (2 * KPL);    // MFMA steps along keys (Oᵀ)
     constexpr int NDB = D / 32;            // 32-dim blocks of O
     constexpr int NF = 16 * NBLK;          // scores per lane per tile
-    constexpr int NG = Groups<T>::value;   // wavefront groups
+    constexpr int NG = Groups<T, CAUSAL>::value;   // wavefront groups
     constexpr int NBUF = 2;                // LDS buffers per operand and group
     constexpr int KD = NBUF == 4 ? 3 : 2;  // step t loads K tile t+KD
     constexpr int VD = NBUF == 4 ? 3 : 1;  // and V tile t+VD
@@ -334,28 +339,23 @@ __global__ __launch_bounds__(kThreads * Groups<T>::value, 2) void attn_fwd_kerne
     }
     const int n_qb = p.cu ? (S + BM - 1) / BM : p.n_qb;
 
-    // With two groups a task is a pair of query blocks of one (batch, query
-    // head): under causal masking the heaviest and the lightest remaining
-    // block (qh = n_qb-1-task, ql = task), otherwise two neighbours.  Group 1
-    // takes the light block and then the first nb key tiles of the heavy
-    // block, group 0 the rest of the heavy block; nb evens out the two
-    // groups' tile counts, and the heavy block's two partial softmax states
-    // are merged through LDS at the end.  With one group a task is one block,
-    // heaviest first for the first half of the launch and lightest first for
-    // the second half (two workgroups per CU even out).  A packed sequence
+    // With two groups (causal masking only) a task is a pair of query blocks
+    // of one (batch, query head): the heaviest and the lightest remaining
+    // block (qh = n_qb-1-task, ql = task).  Group 1 takes the light block and
+    // then the first nb key tiles of the heavy block, group 0 the rest of the
+    // heavy block; nb evens out the two groups' tile counts, and the heavy
+    // block's two partial softmax states are merged through LDS at the end.
+    // With one group a task is one block; under causal masking heaviest
+    // first for the first half of the launch and lightest first for the
+    // second half (two workgroups per CU even out).  A packed sequence
     // shorter than the longest has fewer blocks: its surplus tasks leave here,
     // before any barrier (the whole workgroup shares b and task).
     int qh = task, ql = -1;
     if (NG == 2) {
-        if (CAUSAL) {
-            qh = n_qb - 1 - task;
-            ql = task < qh ? task : -1;
-            if (task > qh) return;
-        } else {
-            qh = 2 * task;
-            ql = 2 * task + 1 < n_qb ? 2 * task + 1 : -1;
-            if (qh >= n_qb) return;
-        }
+        static_assert(!(NG == 2 && !CAUSAL), "two groups only pair causal blocks");
+        qh = n_qb - 1 - task;
+        ql = task < qh ? task : -1;
+        if (task > qh) return;
     } else {
         if (task >= n_qb) return;
         if (CAUSAL) {
@@ -986,7 +986,7 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     kp.rope_lb = a.rope_lb;
     kp.cu = a.cu_seqlens;
     kp.total = int(a.total);
-    constexpr int NG = Groups<T>::value;
+    constexpr int NG = Groups<T, CAUSAL>::value;
     const int n_tasks = NG == 2 ? (kp.n_qb + 1) / 2 : kp.n_qb;
     const int64_t n_wg = int64_t(n_tasks) * kp.n_units;
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD, LSE, ROPE>), dim3(unsigned(n_wg)), dim3(kThreads * NG), 0,
