@@ -181,7 +181,7 @@ struct KParams {
     int total;                      // T (packed sequences; S is then the longest length)
     float sl2;                      // scale * log2(e)
     const int32_t* rope_pos;        // (B, S) positions, or null for 0..S-1
-    double rope_lb;                 // log2 of the rotary base
+    double rope_r1;                 // rho = base^(-2/D): theta_{i+1} / theta_i
 };
 
 // Rotary embedding: cos and sin of position × theta_i, from f = theta_i / 2π.
@@ -531,12 +531,11 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             // position × theta_i; the rotated values are rounded to T, as the
             // MFMA operand.
             const int pos = qrow < S ? (p.rope_pos ? p.rope_pos[int64_t(b) * S + qrow] : qrow) : 0;
-            // theta_i = rho^i with rho = base^(-2/D), formed here from an
-            // opaque copy of log2(base) so that nothing stays live across the
+            // theta_i = rho^i with rho = base^(-2/D) (from the host), read
+            // through an opaque copy so that nothing stays live across the
             // tile loop
-            double lb = p.rope_lb;
-            asm volatile("" : "+v"(lb));
-            const double r1 = exp2(lb * (-2.0 / D));
+            double r1 = p.rope_r1;
+            asm volatile("" : "+v"(r1));
             const double r4 = (r1 * r1) * (r1 * r1);
             const double r8 = r4 * r4;
             if constexpr (KPL == 1) {
@@ -983,7 +982,7 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     kp.kv_bstride = a.S * a.Hkv * a.D;
     kp.sl2 = a.scale * 1.44269504088896340736f;
     kp.rope_pos = a.rope_pos;
-    kp.rope_lb = a.rope_lb;
+    kp.rope_r1 = std::exp2(-2.0 * a.rope_lb / D);
     kp.cu = a.cu_seqlens;
     kp.total = int(a.total);
     constexpr int NG = Groups<T, CAUSAL>::value;
