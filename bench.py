@@ -42,12 +42,23 @@ def metric_flops(w):
     return f / 2.0 if w.causal else f
 
 
+def algorithmic_flops(w, pad):
+    """FLOPs of the scores the method actually computes: with key padding,
+    batch b has L_b visible keys per row (4·H·S·L_b·D), halved under causal
+    masking like the metric's count.  Equals metric_flops without padding."""
+    if pad is None:
+        return metric_flops(w)
+    f = sum(4.0 * w.Hq * w.S * int(min(max(L, 0), w.S)) * w.D for L in pad)
+    return f / 2.0 if w.causal else f
+
+
 def min_hbm_bytes(w, pad):
     """Q, K, V read once, O (and LSE) written once (the score matrix never
-    reaches memory)."""
+    reaches memory); with key padding, K and V rows past L_b are never read."""
     el = {"bf16": 2, "fp16": 2, "fp32": 4}[w.dtype]
     qo = 2 * w.B * w.S * w.Hq * w.D * el
-    kv = 2 * w.B * w.S * w.Hkv * w.D * el
+    rows = w.B * w.S if pad is None else sum(int(min(max(L, 0), w.S)) for L in pad)
+    kv = 2 * rows * w.Hkv * w.D * el
     lse = w.B * w.Hq * w.S * 4 if w.want_lse else 0
     return qo + kv + lse
 
@@ -125,17 +136,22 @@ def run_gpu(w, steps, warmup, use_graph=True, warmup_s=0.0, rope=False):
     return dict(ms_per_step=ms_wall, kernel_ms_mean=ms_dev, pad=pad, warmup_done=done)
 
 
-KERNEL_SOURCES = ["transformer_attention_06_amd/csrc/attn_fwd_kernels.hip",
-                  "transformer_attention_06_amd/csrc/attn_api.cpp"]
-
-
 def kernel_source_sha():
-    import hashlib
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the library's sources as they stand in the tree (the same
+    digest the build embeds in attn_version())."""
+    from transformer_attention_06_amd.build import source_hash
+    return source_hash()
+
+
+def check_library_matches_sources():
+    """Refuse to report numbers for a library built from other sources."""
+    from transformer_attention_06_amd import attn as A
+    built, here = A.library_source_hash(), kernel_source_sha()
+    if built != here:
+        print(f"bench.py: the loaded library was built from sources {built}, the tree holds {here}: "
+              "rebuild (python -m transformer_attention_06_amd.build) before measuring.", file=sys.stderr)
+        sys.exit(3)
+    return here
 
 
 def measured_traffic(name):
@@ -201,11 +217,7 @@ def cpu_baseline(w, budget_s=12.0):
     the time budget is spent; report the metric's unit (TFLOP/s)."""
     import oracle
     from transformer_attention_06_amd import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        threads = 1
+    host = host_info()
     import torch
     q, k, v, pad = W.make_inputs(w)
     dt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
@@ -224,9 +236,39 @@ def cpu_baseline(w, budget_s=12.0):
             break
     el = time.perf_counter() - t0
     flops = metric_flops(w) * done / len(units)
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": host["blas_threads"], "kind": "oracle",
             "sample": f"{done} of {len(units)} (batch, head) units of {w.name}, fp64 numpy, "
-                      f"full SxS score matrix, {el:.2f} s wall"}
+                      f"full SxS score matrix, {el:.2f} s wall",
+            "host": host}
+
+
+def host_info():
+    """The CPU the oracle runs on: model name, the cores this process may use
+    (sched_getaffinity), and the BLAS library numpy calls with its thread
+    count (threadpoolctl)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - not Linux
+        affinity = os.cpu_count() or 1
+    blas, threads = "unknown", 1
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api', '?')} {libs[0].get('version', '?')}"
+            threads = int(libs[0].get("num_threads", 1))
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        pass
+    return {"cpu_model": model, "affinity_cores": affinity, "blas": blas, "blas_threads": threads}
 
 
 DECODE_SHAPES = {
@@ -417,7 +459,16 @@ def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0, rope=
                      # over the kernel time), for shapes near the ridge
                      "hbm_frac": round(min_hbm_bytes(w, r["pad"]) / (r["kernel_ms_mean"] * 1e-3) / 1e9
                                        / HBM_PEAK_GBS, 4)},
+        "source_sha": kernel_source_sha(),
     }
+    if r["pad"] is not None:
+        # key padding: the metric counts every key (dense S x S, as the
+        # metric's definition states); the method computes only the visible
+        # ones (sum over b of 4 H S L_b D)
+        afl = algorithmic_flops(w, r["pad"])
+        line["roofline"]["algorithmic_flops_per_launch"] = afl
+        line["roofline"]["algorithmic_tflops"] = round(afl / (r["kernel_ms_mean"] * 1e-3) / 1e12, 3)
+        line["roofline"]["algorithmic_frac"] = round(afl / (r["kernel_ms_mean"] * 1e-3) / 1e12 / peak, 4)
     if rope:
         # the call is two launches: the K rotation pass (bandwidth-bound: K
         # read and written once) and the attention with Q rotated at load;
@@ -485,6 +536,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    check_library_matches_sources()
     if args.decode:
         for name in DECODE_SHAPES:
             print(json.dumps(bench_decode(name, args.steps, args.warmup, not args.no_graph, warmup_s)), flush=True)

@@ -289,7 +289,9 @@ int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_heads, int64_
 /* Static, human-readable text for a return code (never NULL). */
 const char* attn_strerror(int code);
 
-/* Library version string, e.g. "attn_fwd 0.1.0 gfx950". */
+/* Library version string, e.g. "attn_fwd 0.2.0 gfx950 src 0123456789abcdef":
+ * the last word is the first 16 hex digits of the SHA-256 of the sources the
+ * library was built from (static storage, never NULL). */
 const char* attn_version(void);
 
 #ifdef __cplusplus

@@ -51,6 +51,14 @@ def test_version_and_strerror(lib):
     assert A.strerror(-1234) == "unknown error code"
 
 
+def test_library_built_from_the_tree(lib):
+    """attn_version() names the sources the library was built from; the
+    library under test must come from the sources in this tree."""
+    from transformer_attention_06_amd.build import source_hash
+    assert re.fullmatch(r"[0-9a-f]{16}", A.library_source_hash())
+    assert A.library_source_hash() == source_hash()
+
+
 FAKE = 0x10000  # a 16-byte aligned non-NULL address that is never dereferenced
 
 

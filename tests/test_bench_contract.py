@@ -40,3 +40,22 @@ def test_metric_counts_for_the_benchmark_workload():
     assert bench.metric_flops(w) == 4 * 1 * 32 * 2048 ** 2 * 128 / 2 == 34359738368
     # Q, K, V read once and O written once, bf16: 4 · 2048 · 32 · 128 · 2 B = 64 MiB
     assert bench.min_hbm_bytes(w, None) == 64 * 2 ** 20
+
+
+def test_padded_workload_algorithmic_counts():
+    """Key padding: the metric keeps the dense count; the algorithmic FLOPs
+    and bytes count only the L_b visible keys of each batch entry."""
+    w = W.WORKLOADS["batched_padded"]
+    pad = [128, 512] + [320] * (w.B - 2)
+    dense = bench.metric_flops(w)
+    assert dense == 4 * w.B * w.Hq * w.S ** 2 * w.D
+    assert bench.algorithmic_flops(w, pad) == sum(4 * w.Hq * w.S * L * w.D for L in pad)
+    el = 2
+    assert bench.min_hbm_bytes(w, pad) == 2 * w.B * w.S * w.Hq * w.D * el + 2 * sum(pad) * w.Hkv * w.D * el
+    assert bench.algorithmic_flops(w, None) == dense
+
+
+def test_host_info_names_the_cpu():
+    h = bench.host_info()
+    assert h["affinity_cores"] >= 1 and h["blas_threads"] >= 1
+    assert isinstance(h["cpu_model"], str) and isinstance(h["blas"], str)

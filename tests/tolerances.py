@@ -40,7 +40,8 @@ def lse_error(lse, ref):
     ref = np.asarray(ref, dtype=np.float64)
     both_ninf = np.isneginf(lse) & np.isneginf(ref)
     assert np.array_equal(np.isneginf(lse), np.isneginf(ref)), "rows with no visible key differ"
-    d = np.where(both_ninf, 0.0, np.abs(lse - ref))
+    # subtract only where the rows are not both -inf (inf - inf is NaN)
+    d = np.abs(np.subtract(lse, ref, out=np.zeros_like(lse), where=~both_ninf))
     assert np.all(np.isfinite(d)), "non-finite LSE"
     return float(d.max()) if d.size else 0.0
 

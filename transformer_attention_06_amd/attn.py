@@ -97,6 +97,12 @@ def version():
     return load_library().attn_version().decode()
 
 
+def library_source_hash():
+    """Hash of the sources the loaded library was built from (the last word
+    of attn_version())."""
+    return version().rsplit(" ", 1)[-1]
+
+
 class AttnError(RuntimeError):
     def __init__(self, code):
         self.code = code

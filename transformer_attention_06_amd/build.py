@@ -3,6 +3,7 @@
     python -m transformer_attention_06_amd.build [--verbose]
 """
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -17,6 +18,23 @@ LIB = os.path.join(PKG, "libattn_fwd.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", "attn_decode_kernels.hip", "attn_masked_kernels.hip"]
+
+
+def source_hash():
+    """First 16 hex digits of the SHA-256 over every source the library is
+    built from (csrc/ and the public header, in name order).  The build
+    embeds it in attn_version(), so a loaded library names the sources it
+    came from."""
+    h = hashlib.sha256()
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                   if f.endswith((".hip", ".cpp", ".h")))
+    files.append(os.path.join(INCLUDE, "attn_fwd.h"))
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
 
 # Packed-fp32 VALU forms are kept out of the device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -36,7 +54,7 @@ def build(verbose=False, extra_flags=()):
     (asm_check); the library is only installed if that check passes."""
     tmp = LIB + ".tmp"
     common = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
-              *DEVICE_FLAGS, *extra_flags]
+              f'-DATTN_SRC_HASH="{source_hash()}"', *DEVICE_FLAGS, *extra_flags]
     with tempfile.TemporaryDirectory() as td:
         objs, procs = [], []
         for src in SOURCES:

@@ -323,4 +323,10 @@ extern "C" const char* attn_strerror(int code) {
     }
 }
 
-extern "C" const char* attn_version(void) { return "attn_fwd 0.1.0 gfx950"; }
+#ifndef ATTN_SRC_HASH
+#define ATTN_SRC_HASH "unknown"
+#endif
+
+// The version string ends with the hash of the sources the library was built
+// from (set by the build), so a caller can tell which sources it runs.
+extern "C" const char* attn_version(void) { return "attn_fwd 0.2.0 gfx950 src " ATTN_SRC_HASH; }

@@ -927,6 +927,12 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     // m = max(m0, m1), O = O0·2^(m0-m) + O1·2^(m1-m), likewise the sums.
     if constexpr (NG == 2) {
         if (nb > 0) {
+            // The last step of each segment ends without a barrier, and the
+            // padding above adds none to the group with the most barriers:
+            // wait until every wavefront has finished reading its tiles
+            // before group 1 overwrites its own tile region (nb is uniform
+            // over the workgroup, so all eight wavefronts arrive here).
+            __syncthreads();
             constexpr int GRP_E = 2 * NBUF * TILE_E;  // elements per group region
             float* stash_o = reinterpret_cast<float*>(lds + GRP_E);
             float* stash_s = reinterpret_cast<float*>(lds);  // m, l, l_lse (group 0's region)
