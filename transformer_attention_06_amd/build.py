@@ -18,6 +18,8 @@ LIB = os.path.join(PKG, "libattn_fwd.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", "attn_decode_kernels.hip", "attn_masked_kernels.hip"]
+# kernels whose MFMAs are inline assembly: their device assembly is checked
+ASM_CHECKED = ["attn_fwd_kernels.hip"]
 
 
 def source_hash():
@@ -63,10 +65,13 @@ def build(verbose=False, extra_flags=()):
             cmd = [hipcc(), *common, "-c", "-Wall", "-Wno-unused-result", "-Wno-pass-failed", "-o", obj,
                    os.path.join(CSRC, src)]
             procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
-        asm = os.path.join(td, "kernels.s")
-        acmd = [hipcc(), *common, "--cuda-device-only", "-S", "-Wno-pass-failed", "-o", asm,
-                os.path.join(CSRC, "attn_fwd_kernels.hip")]
-        procs.append((acmd, subprocess.Popen(acmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        asms = []
+        for src in ASM_CHECKED:
+            asm = os.path.join(td, os.path.splitext(src)[0] + ".s")
+            asms.append(asm)
+            acmd = [hipcc(), *common, "--cuda-device-only", "-S", "-Wno-pass-failed", "-o", asm,
+                    os.path.join(CSRC, src)]
+            procs.append((acmd, subprocess.Popen(acmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
         for cmd, pr in procs:
             out, err = pr.communicate()
             if verbose:
@@ -86,8 +91,10 @@ def build(verbose=False, extra_flags=()):
             import asm_check
         finally:
             sys.path.pop(0)
-        with open(asm) as f:
-            problems = asm_check.check_asm(f.read())
+        problems = []
+        for asm in asms:
+            with open(asm) as f:
+                problems += asm_check.check_asm(f.read())
     if problems:
         os.remove(tmp)
         raise RuntimeError("MFMA wait-state check failed:\n" + "\n".join(problems[:20]))

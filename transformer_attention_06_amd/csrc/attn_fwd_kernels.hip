@@ -39,210 +39,14 @@
 #include <type_traits>
 
 #include "attn_fwd.h"
+#include "attn_fwd_common.h"
 #include "attn_launch.h"
 
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kThreads = 256;
 constexpr int BM = attn_detail::kBlockM;  // 128 query rows per workgroup
 static_assert(BM == 4 * 32, "4 wavefronts x 32 rows");
-
-template <typename T>
-struct Elem;
-template <>
-struct Elem<__bf16> {
-    static constexpr int KPL = 8;  // operand elements per lane per MFMA
-    static constexpr int BN = 64;  // keys per K/V tile
-    using op_t = bf16x8;
-};
-template <>
-struct Elem<_Float16> {
-    static constexpr int KPL = 8;
-    static constexpr int BN = 64;
-    using op_t = f16x8;
-};
-template <>
-struct Elem<float> {
-    static constexpr int KPL = 1;
-    static constexpr int BN = 32;
-    using op_t = float;
-};
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
-// The same products as ordered inline assembly: the tile loop issues its
-// MFMAs, operand reads and VALU work in a fixed interleaved order, and
-// assembly statements are never reordered against each other or against
-// memory operations.  "+v" accumulates in place; the zero-start form writes a
-// fresh accumulator (early-clobber: no overlap with the operands).
-__device__ __forceinline__ void mfma_acc(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_acc(f32x16& c, const f16x8& a, const f16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-}
-// fp32 (a parity path, at the register limit at D = 128): the compiler's
-// own MFMA, so that its hazard tracking covers any copy it inserts
-__device__ __forceinline__ void mfma_acc(f32x16& c, const float& a, const float& b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void mfma_zero(f32x16& c, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_zero(f32x16& c, const f16x8& a, const f16x8& b) {
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_zero(f32x16& c, const float& a, const float& b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, f32x16{}, 0, 0, 0);
-}
-// Empty assembly statements that fix where VALU work happens in the stream:
-// keep() marks values as needed at this point (computed no later); touch()
-// marks a value as redefined here (work using it starts no earlier).
-__device__ __forceinline__ void keep(float x) { asm volatile("" : : "v"(x)); }
-__device__ __forceinline__ void touch(float& x) { asm volatile("" : "+v"(x)); }
-
-template <typename OP, typename T>
-__device__ __forceinline__ OP load_op(const T* p) {
-    return *reinterpret_cast<const OP*>(p);
-}
-
-// Combine a value with the one held by lane l^32 (the other half of the
-// same query row): one cross-half swap instead of an LDS permute.
-__device__ __forceinline__ float max_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_xor32(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// The running max is only raised when a row's new tile max exceeds it by
-// more than this many powers of two; otherwise the stale max is kept, the
-// exponentials stay below 2^8 and the output accumulator needs no rescale.
-constexpr float kRescaleLog2 = 8.0f;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// Transposing LDS read: in each 16-lane group, lane 4j+q names an 8-byte
-// piece (4 elements of one row); lane 4q+c receives element c of the pieces
-// named by lanes 4j+q, j = 0..3 (a 4-row × 16-column block, transposed).
-__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
-    typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(p));
-}
-
-// Sum of the two 16-bit probabilities in a packed pair, accumulated in fp32
-// (dot product with (1, 1)): the row sum is taken over exactly the rounded
-// values that enter the P·V product.
-__device__ __forceinline__ float sum2(bf16x2 p, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(p, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
-}
-__device__ __forceinline__ float sum2(f16x2 p, float acc) {
-    return __builtin_amdgcn_fdot2(p, f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
-}
-
-// A-operand row permutation: swap bits 2 and 3 of a 0..31 row index.
-__device__ __forceinline__ int perm_row(int r) {
-    return (r & 0x13) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
-// Position (key within the tile, or head dim within a 32-wide block pair)
-// held by accumulator register f (0..16*blocks-1) of a lane in half g.
-__host__ __device__ constexpr int kidx(int f, int g) {
-    return 32 * (f >> 4) + 16 * ((f >> 3) & 1) + 8 * g + (f & 7);
-}
-
-struct KParams {
-    const void* q;
-    const void* k;
-    const void* v;
-    void* o;
-    float* lse;
-    const int32_t* pad_lens;
-    int S, Hq, Hkv, group, n_qb, n_units, xcd_chunk;
-    int64_t q_bstride, kv_bstride;  // elements per batch
-    const int32_t* cu;              // packed sequences: offsets cu[0..B] into T rows, or null
-    int total;                      // T (packed sequences; S is then the longest length)
-    float sl2;                      // scale * log2(e)
-    const int32_t* rope_pos;        // (B, S) positions, or null for 0..S-1
-    double rope_r1;                 // rho = base^(-2/D): theta_{i+1} / theta_i
-};
-
-// Rotary embedding: cos and sin of position × theta_i, from f = theta_i / 2π.
-// The angle in turns is reduced to [-1/2, 1/2] in fp64, which is exact
-// enough for any int32 position; the 16-bit types then use the hardware sine
-// and cosine of a turn count (their error is far below the rounding of the
-// rotated value to 16 bits), fp32 the full-precision library sincos.
-template <typename T>
-__device__ __forceinline__ void rope_cs(int pos, double f, float& c, float& s) {
-    const double turns = double(pos) * f;
-    const double r = turns - __builtin_rint(turns);
-    if constexpr (sizeof(T) == 2) {
-        const float rf = float(r);
-        s = __builtin_amdgcn_sinf(rf);
-        c = __builtin_amdgcn_cosf(rf);
-    } else {
-        sincosf(float(r * 6.283185307179586476925), &s, &c);
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ T to_t(float x) {
-    return static_cast<T>(x);
-}
-
-// XOR swizzle of the 16-byte slots of a K/V tile row (NS slots per row).
-// With 64 LDS banks, this makes the three access patterns of the kernel
-// conflict-free: 16-lane row writes, the K-operand reads (16 permuted rows,
-// one slot each) and the transposing V reads (4 consecutive rows, 32 bytes
-// each, two 16-lane groups side by side).
-template <int NS>
-__device__ __forceinline__ int swz(int row) {
-    if constexpr (NS >= 16)
-        return ((row & 3) << 2) | ((row >> 2) & 3);
-    else
-        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource words for [base, base + bytes) (gfx9 default data format);
-// loads at offsets at or past the end return zero.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xffff), int(bytes), 0x00020000};
-}
-
-// One 16-byte global load per lane, written to LDS at lds_byte + 16·lane
-// (buffer_load_dwordx4 with LDS destination; M0 holds the LDS address).
-// Issued as inline assembly on purpose: the compiler then does not track
-// these LDS writes and inserts no waits for them before unrelated LDS reads
-// (it cannot prove the tile being read differs from the tile being loaded).
-// Every read of a loaded tile is ordered explicitly instead: the loading
-// wave waits vmcnt(0), then a workgroup barrier.  No other code in the kernel
-// uses M0.
-__device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t lds_byte, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_byte), "v"(voff), "s"(rs)
-                 : "memory");
-}
 
 // Wavefront groups per workgroup: two for the 16-bit types under causal
 // masking (eight wavefronts, two per SIMD, a heavy and a light query block
@@ -300,8 +104,11 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     static_assert(NBUF * TILE_E * ES <= 65536, "buffer offsets fit the LDS immediate");
 
     // Per group: K tiles [NBUF][BN][D], then V tiles [NBUF][BN][D], slots
-    // swizzled.
-    __shared__ __attribute__((aligned(1024))) T lds[NG * 2 * NBUF * TILE_E];
+    // swizzled.  With two groups, one more region holds the Q rows of the
+    // heavy block for group 1's second segment ([BM][D], slots swizzled like
+    // a tile), loaded while its first segment runs.
+    constexpr int QPF_E = NG == 2 ? BM * D : 0;
+    __shared__ __attribute__((aligned(1024))) T lds[NG * 2 * NBUF * TILE_E + QPF_E];
 
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
@@ -486,6 +293,45 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             load_part(tile_rsrc(vaddr, tv), lds_v_s, vbuf, i - NLD);
     };
 
+    // Group 1 with two segments (the light block, then the first nb key tiles
+    // of the heavy block) prepares the second while the first runs: the heavy
+    // block's Q rows go to the Q region by direct loads (issued once the first
+    // segment's tiles are in), its first two K tiles to K buffers 0 and 1
+    // during the first segment's last step (which reads no K buffer).  The
+    // second segment then starts without waiting for HBM.
+    const bool prep2 = NG == 2 && grp == 1 && ql >= 0 && nb > 0;
+    constexpr int NLDQ = BM * ROW_B / 4096;  // 1 KiB Q loads per wave
+    static_assert(NG == 1 || NLDQ * 4096 == BM * ROW_B, "Q block split into 1 KiB wave loads");
+    auto load_q_next = [&](int li) __attribute__((always_inline)) {
+        // rows qh·BM .. qh·BM+BM-1 of this (batch, query head); rows past S
+        // read as zero
+        const int r0 = qh * BM;
+        const uint32_t qrow_b = uint32_t(qstride * int64_t(ES));
+        const int64_t valid = int64_t(S - r0) * qstride - (qstride - D);  // elements through row S-1
+        const uint32_t qbytes = valid > 0 ? uint32_t(valid * ES) : 0u;
+        const uint64_t qa = reinterpret_cast<uint64_t>(qbase + int64_t(r0) * qstride);
+        const i32x4 rs{__builtin_amdgcn_readfirstlane(int(uint32_t(qa))),
+                       __builtin_amdgcn_readfirstlane(int(uint32_t(qa >> 32) & 0xffff)),
+                       __builtin_amdgcn_readfirstlane(int(qbytes)), 0x00020000};
+        const int rw = (w4 * NLDQ + li) * RPL;
+        uint32_t lb = uint32_t(lr) * qrow_b + uint32_t((ps ^ swz<NS>(lr)) * 16);
+        asm volatile("" : "+v"(lb));
+        const uint32_t voff = (lb ^ uint32_t(swz<NS>(rw) * 16)) + uint32_t(rw) * qrow_b;
+        const uint32_t lq = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds + NG * 2 * NBUF * TILE_E)));
+        lds_dma16(rs, lq + uint32_t((w4 * NLDQ + li) * 1024), voff);
+    };
+    // K tile i/NLD (0 or 1) of the second segment, load i%NLD, into K buffer i/NLD
+    auto load_k_next = [&](int i) __attribute__((always_inline)) {
+        const int t = i / NLD;
+        const uint32_t off = uint32_t(t * BN) * row_bytes;
+        const bool live = t < seg_b1 && off < kv_bytes;
+        const uint64_t a = kaddr + off;
+        const i32x4 rs{__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
+                       __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff)),
+                       __builtin_amdgcn_readfirstlane(int(live ? kv_bytes - off : 0u)), 0x00020000};
+        load_part(rs, lds_k_s, t, i % NLD);
+    };
+
     // ---- per-lane LDS read offsets (elements, within a tile) ---------------
     const int prow = perm_row(r);
     const int xk = swz<NS>(prow);  // swizzle of every K row this lane reads (row ≡ prow mod 16)
@@ -514,10 +360,19 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     float m_run = -INFINITY;  // running max (scaled, log2)
     float l_run = 0.0f;       // sum of the rounded probabilities
     float l_lse = 0.0f;       // sum of the exact probabilities (LSE)
-    auto begin_rows = [&](int q) __attribute__((always_inline)) {
+    auto begin_rows = [&](int q, bool q_in_lds) __attribute__((always_inline)) {
         wrow0 = q * BM + w4 * 32;
         qrow = wrow0 + r;
-        if (qrow < S) {
+        if (NG == 2 && q_in_lds) {
+            // the prefetched block: row w4·32 + r of the Q region (zero past S)
+            const T* qs = lds + NG * 2 * NBUF * TILE_E + (w4 * 32 + r) * D;
+            const int xq = swz<NS>(w4 * 32 + r);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int col = c * 2 * KPL + gl * KPL;
+                qv[c] = load_op<op_t>(qs + (((col / CH) ^ xq) * CH) + col % CH);
+            }
+        } else if (qrow < S) {
             const T* qr = qbase + int64_t(qrow) * qstride;
 #pragma unroll
             for (int c = 0; c < NC; ++c) qv[c] = load_op<op_t>(qr + c * 2 * KPL + gl * KPL);
@@ -762,7 +617,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     // 1 - par, V tile t in V buffer par, and this step loads K tile t+2 into
     // K buffer par and V tile t+1 into V buffer 1 - par.
     auto step = [&](const int t, const int par, f32x16 (&sc)[NBLK], f32x16 (&sn)[NBLK],
-                    const bool G1) __attribute__((always_inline)) {
+                    const bool G1, const bool pf_next = false) __attribute__((always_inline)) {
         const T* kn = lds_k + (1 - par) * TILE_E;
         const T* vc = lds_v + par * TILE_E;
         constexpr int NL = 2 * NLD;
@@ -778,6 +633,9 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
         // part A
 #pragma unroll
         for (int i = 0; i < N1; ++i) {
+            // the last step loads no tile of its own; when the group has a
+            // second segment, it loads that segment's first two K tiles
+            if (!G1 && pf_next && i % (N1 / NL) == 0) load_k_next(i / (N1 / NL));
             if (G1) {
                 if (i % (N1 / NL) == 0) load_one(t + KD, t + VD, par, 1 - par, i / (N1 / NL));
                 if (i + PF < N1 + N2) fetch(i + PF);
@@ -844,24 +702,41 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
         const int t1 = sg == 0 ? seg_b0 : seg_b1;
         const bool out = sg == 0 ? seg_out0 : seg_out1;
         seg_end = t1;
+        // the second segment of a prepared group: Q in LDS, K tiles t0, t0+1
+        // already loaded (t0 = 0)
+        const bool prepared = sg > 0 && prep2;
         if (sg > 0) {  // the previous segment's last step may still read the buffers
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the prepared Q rows and K tiles landed
             __syncthreads();
             ++n_bar;
         }
-        begin_rows(q);
+        begin_rows(q, prepared);
         if (t0 < t1) {
             // prologue: K tiles t0..t0+KD-1, V tiles t0..t0+VD-1 resident, Sᵀ(t0)
+            if (!prepared) {
 #pragma unroll
-            for (int k = 0; k < KD; ++k)
+                for (int k = 0; k < KD; ++k)
 #pragma unroll
-                for (int i = 0; i < NLD; ++i) load_one(t0 + k, 0, k, 0, i);
+                    for (int i = 0; i < NLD; ++i) load_one(t0 + k, 0, k, 0, i);
+            }
 #pragma unroll
             for (int k = 0; k < VD; ++k)
 #pragma unroll
                 for (int i = NLD; i < 2 * NLD; ++i) load_one(0, t0 + k, 0, k, i);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
+            if (prepared) {
+                // Sᵀ(t0) needs only K tile t0 (landed before the segment
+                // barrier); the V tile is waited for after the product
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
+            }
             __syncthreads();
             ++n_bar;
+            // group 1 with a second segment: the heavy block's Q rows to LDS,
+            // in flight behind the first segment's work
+            if (sg == 0 && prep2) {
+#pragma unroll
+                for (int i = 0; i < NLDQ; ++i) load_q_next(i);
+            }
             {
                 const T* k0 = lds_k;
                 op_t fr[PF + 1];
@@ -881,7 +756,10 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             // the MFMA result latency (the products are assembly, so the
             // compiler does not insert these wait states itself)
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-            // step t0 reloads the buffer K tile t0 was read from
+            // the prepared segment's V tile t0 (and, in the first segment of
+            // a group with two, nothing else: the Q prefetch may stay in
+            // flight); step t0 reloads the buffer K tile t0 was read from
+            if (prepared) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             __syncthreads();
             ++n_bar;
             mask_tile(sa, t0);
@@ -910,8 +788,9 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
                     sa[blk] = sb[blk];
                 }
             }
-            // last step (t = t1-1): no next tile
-            step(t, (t - t0) & 1, sa, sb, false);
+            // last step (t = t1-1): no next tile; in a group's first of two
+            // segments, it loads the second segment's first K tiles
+            step(t, (t - t0) & 1, sa, sb, false, sg == 0 && prep2);
             // the output accumulators were last written by MFMAs issued just
             // now (wait states as after the prologue)
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
