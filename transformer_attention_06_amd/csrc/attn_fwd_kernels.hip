@@ -104,11 +104,8 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     static_assert(NBUF * TILE_E * ES <= 65536, "buffer offsets fit the LDS immediate");
 
     // Per group: K tiles [NBUF][BN][D], then V tiles [NBUF][BN][D], slots
-    // swizzled.  With two groups, one more region holds the Q rows of the
-    // heavy block for group 1's second segment ([BM][D], slots swizzled like
-    // a tile), loaded while its first segment runs.
-    constexpr int QPF_E = NG == 2 ? BM * D : 0;
-    __shared__ __attribute__((aligned(1024))) T lds[NG * 2 * NBUF * TILE_E + QPF_E];
+    // swizzled.
+    __shared__ __attribute__((aligned(1024))) T lds[NG * 2 * NBUF * TILE_E];
 
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
@@ -186,7 +183,11 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     const int Th = tiles_of(qh);
     const int Tl = tiles_of(ql);
     int nb = 0;
-    if (NG == 2) nb = ql >= 0 ? (Th > Tl ? (Th - Tl) / 2 : 0) : Th / 2;
+    // Both groups pass the same barriers, one per step, so the work is
+    // balanced by barrier count: group 0 passes Th - nb + 1, group 1 (light
+    // block, then the heavy block's first nb tiles, one barrier between)
+    // Tl + nb + 3.
+    if (NG == 2) nb = ql >= 0 ? (Th - Tl > 2 ? (Th - Tl - 2) / 2 : 0) : Th / 2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -293,45 +294,6 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             load_part(tile_rsrc(vaddr, tv), lds_v_s, vbuf, i - NLD);
     };
 
-    // Group 1 with two segments (the light block, then the first nb key tiles
-    // of the heavy block) prepares the second while the first runs: the heavy
-    // block's Q rows go to the Q region by direct loads (issued once the first
-    // segment's tiles are in), its first two K tiles to K buffers 0 and 1
-    // during the first segment's last step (which reads no K buffer).  The
-    // second segment then starts without waiting for HBM.
-    const bool prep2 = NG == 2 && grp == 1 && ql >= 0 && nb > 0;
-    constexpr int NLDQ = BM * ROW_B / 4096;  // 1 KiB Q loads per wave
-    static_assert(NG == 1 || NLDQ * 4096 == BM * ROW_B, "Q block split into 1 KiB wave loads");
-    auto load_q_next = [&](int li) __attribute__((always_inline)) {
-        // rows qh·BM .. qh·BM+BM-1 of this (batch, query head); rows past S
-        // read as zero
-        const int r0 = qh * BM;
-        const uint32_t qrow_b = uint32_t(qstride * int64_t(ES));
-        const int64_t valid = int64_t(S - r0) * qstride - (qstride - D);  // elements through row S-1
-        const uint32_t qbytes = valid > 0 ? uint32_t(valid * ES) : 0u;
-        const uint64_t qa = reinterpret_cast<uint64_t>(qbase + int64_t(r0) * qstride);
-        const i32x4 rs{__builtin_amdgcn_readfirstlane(int(uint32_t(qa))),
-                       __builtin_amdgcn_readfirstlane(int(uint32_t(qa >> 32) & 0xffff)),
-                       __builtin_amdgcn_readfirstlane(int(qbytes)), 0x00020000};
-        const int rw = (w4 * NLDQ + li) * RPL;
-        uint32_t lb = uint32_t(lr) * qrow_b + uint32_t((ps ^ swz<NS>(lr)) * 16);
-        asm volatile("" : "+v"(lb));
-        const uint32_t voff = (lb ^ uint32_t(swz<NS>(rw) * 16)) + uint32_t(rw) * qrow_b;
-        const uint32_t lq = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds + NG * 2 * NBUF * TILE_E)));
-        lds_dma16(rs, lq + uint32_t((w4 * NLDQ + li) * 1024), voff);
-    };
-    // K tile i/NLD (0 or 1) of the second segment, load i%NLD, into K buffer i/NLD
-    auto load_k_next = [&](int i) __attribute__((always_inline)) {
-        const int t = i / NLD;
-        const uint32_t off = uint32_t(t * BN) * row_bytes;
-        const bool live = t < seg_b1 && off < kv_bytes;
-        const uint64_t a = kaddr + off;
-        const i32x4 rs{__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
-                       __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff)),
-                       __builtin_amdgcn_readfirstlane(int(live ? kv_bytes - off : 0u)), 0x00020000};
-        load_part(rs, lds_k_s, t, i % NLD);
-    };
-
     // ---- per-lane LDS read offsets (elements, within a tile) ---------------
     const int prow = perm_row(r);
     const int xk = swz<NS>(prow);  // swizzle of every K row this lane reads (row ≡ prow mod 16)
@@ -360,19 +322,10 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     float m_run = -INFINITY;  // running max (scaled, log2)
     float l_run = 0.0f;       // sum of the rounded probabilities
     float l_lse = 0.0f;       // sum of the exact probabilities (LSE)
-    auto begin_rows = [&](int q, bool q_in_lds) __attribute__((always_inline)) {
+    auto begin_rows = [&](int q) __attribute__((always_inline)) {
         wrow0 = q * BM + w4 * 32;
         qrow = wrow0 + r;
-        if (NG == 2 && q_in_lds) {
-            // the prefetched block: row w4·32 + r of the Q region (zero past S)
-            const T* qs = lds + NG * 2 * NBUF * TILE_E + (w4 * 32 + r) * D;
-            const int xq = swz<NS>(w4 * 32 + r);
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int col = c * 2 * KPL + gl * KPL;
-                qv[c] = load_op<op_t>(qs + (((col / CH) ^ xq) * CH) + col % CH);
-            }
-        } else if (qrow < S) {
+        if (qrow < S) {
             const T* qr = qbase + int64_t(qrow) * qstride;
 #pragma unroll
             for (int c = 0; c < NC; ++c) qv[c] = load_op<op_t>(qr + c * 2 * KPL + gl * KPL);
@@ -617,7 +570,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     // 1 - par, V tile t in V buffer par, and this step loads K tile t+2 into
     // K buffer par and V tile t+1 into V buffer 1 - par.
     auto step = [&](const int t, const int par, f32x16 (&sc)[NBLK], f32x16 (&sn)[NBLK],
-                    const bool G1, const bool pf_next = false) __attribute__((always_inline)) {
+                    const bool G1) __attribute__((always_inline)) {
         const T* kn = lds_k + (1 - par) * TILE_E;
         const T* vc = lds_v + par * TILE_E;
         constexpr int NL = 2 * NLD;
@@ -633,9 +586,6 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
         // part A
 #pragma unroll
         for (int i = 0; i < N1; ++i) {
-            // the last step loads no tile of its own; when the group has a
-            // second segment, it loads that segment's first two K tiles
-            if (!G1 && pf_next && i % (N1 / NL) == 0) load_k_next(i / (N1 / NL));
             if (G1) {
                 if (i % (N1 / NL) == 0) load_one(t + KD, t + VD, par, 1 - par, i / (N1 / NL));
                 if (i + PF < N1 + N2) fetch(i + PF);
@@ -702,41 +652,24 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
         const int t1 = sg == 0 ? seg_b0 : seg_b1;
         const bool out = sg == 0 ? seg_out0 : seg_out1;
         seg_end = t1;
-        // the second segment of a prepared group: Q in LDS, K tiles t0, t0+1
-        // already loaded (t0 = 0)
-        const bool prepared = sg > 0 && prep2;
         if (sg > 0) {  // the previous segment's last step may still read the buffers
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the prepared Q rows and K tiles landed
             __syncthreads();
             ++n_bar;
         }
-        begin_rows(q, prepared);
+        begin_rows(q);
         if (t0 < t1) {
             // prologue: K tiles t0..t0+KD-1, V tiles t0..t0+VD-1 resident, Sᵀ(t0)
-            if (!prepared) {
 #pragma unroll
-                for (int k = 0; k < KD; ++k)
+            for (int k = 0; k < KD; ++k)
 #pragma unroll
-                    for (int i = 0; i < NLD; ++i) load_one(t0 + k, 0, k, 0, i);
-            }
+                for (int i = 0; i < NLD; ++i) load_one(t0 + k, 0, k, 0, i);
 #pragma unroll
             for (int k = 0; k < VD; ++k)
 #pragma unroll
                 for (int i = NLD; i < 2 * NLD; ++i) load_one(0, t0 + k, 0, k, i);
-            if (prepared) {
-                // Sᵀ(t0) needs only K tile t0 (landed before the segment
-                // barrier); the V tile is waited for after the product
-            } else {
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
-            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
             __syncthreads();
             ++n_bar;
-            // group 1 with a second segment: the heavy block's Q rows to LDS,
-            // in flight behind the first segment's work
-            if (sg == 0 && prep2) {
-#pragma unroll
-                for (int i = 0; i < NLDQ; ++i) load_q_next(i);
-            }
             {
                 const T* k0 = lds_k;
                 op_t fr[PF + 1];
@@ -756,10 +689,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             // the MFMA result latency (the products are assembly, so the
             // compiler does not insert these wait states itself)
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
-            // the prepared segment's V tile t0 (and, in the first segment of
-            // a group with two, nothing else: the Q prefetch may stay in
-            // flight); step t0 reloads the buffer K tile t0 was read from
-            if (prepared) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            // step t0 reloads the buffer K tile t0 was read from
             __syncthreads();
             ++n_bar;
             mask_tile(sa, t0);
@@ -788,9 +718,8 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
                     sa[blk] = sb[blk];
                 }
             }
-            // last step (t = t1-1): no next tile; in a group's first of two
-            // segments, it loads the second segment's first K tiles
-            step(t, (t - t0) & 1, sa, sb, false, sg == 0 && prep2);
+            // last step (t = t1-1): no next tile
+            step(t, (t - t0) & 1, sa, sb, false);
             // the output accumulators were last written by MFMAs issued just
             // now (wait states as after the prologue)
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
