@@ -96,7 +96,9 @@ enum {
     ATTN_ERR_LAUNCH = -8,      /* the HIP launch failed                        */
     ATTN_ERR_DEVICE = -9,      /* the current device is not gfx950             */
     ATTN_ERR_ALIAS = -10,      /* attn_fwd_rope: k_rot overlaps another tensor */
-    ATTN_ERR_WORKSPACE = -11   /* attn_fwd_decode: workspace too small         */
+    ATTN_ERR_WORKSPACE = -11,  /* attn_fwd_decode: workspace too small         */
+    ATTN_ERR_SCRATCH = -12     /* attn_fwd_decode_noalloc: sizes exceed its    *
+                                * fixed workspace (32 MiB per GPU)              */
 };
 
 /*
@@ -280,6 +282,25 @@ int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_cache, const 
                     const int32_t* cache_lens, float scale, int causal, int n_q_heads, int n_kv_heads,
                     const attn_tensor_t* out, float* lse, void* workspace, int64_t workspace_bytes,
                     void* stream);
+
+/*
+ * attn_fwd_decode_noalloc — attn_fwd_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, checks, kernels and results as
+ * attn_fwd_decode, minus the workspace: the per-chunk partial results go to a
+ * fixed array inside the library, 32 MiB on each GPU it runs on, held until
+ * the process ends.  Calls whose attn_decode_workspace_bytes(...) exceeds
+ * 33554432 return ATTN_ERR_SCRATCH (before any HIP call).  The array's device
+ * address is looked up (no allocation) on the first call on each device.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind; each call writes every entry it reads, so nothing needs clearing.
+ * Calls that may overlap on one GPU (concurrent streams, threads) race on the
+ * array: serialise them.  Nothing is allocated or freed by this call.
+ */
+int attn_fwd_decode_noalloc(const attn_tensor_t* q, const attn_tensor_t* k_cache, const attn_tensor_t* v_cache,
+                            const int32_t* cache_lens, float scale, int causal, int n_q_heads, int n_kv_heads,
+                            const attn_tensor_t* out, float* lse, void* stream);
 
 /* Bytes of workspace attn_fwd_decode needs for these sizes: one 256-key chunk
  * (at least one, also for an empty cache) × B·Hq·Sq rows × (D + 3) floats;

@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_strerror(lib):
     assert A.version().startswith("attn_fwd ")
     assert "gfx950" in A.version()
-    for code in range(-11, 1):
+    for code in range(-12, 1):
         assert A.strerror(code)
     assert A.strerror(-1234) == "unknown error code"
 
@@ -254,6 +254,37 @@ def test_decode_empty_queries_return_ok_without_launch(lib):
     assert call_dec(lib, T(S=0, H=8), T(S=100, H=2), T(S=100, H=2), T(S=0, H=8)) == A.ATTN_OK
     assert call_dec(lib, T(B=0, S=1, H=8, data=0), T(B=0, S=5, H=2, data=0), T(B=0, S=5, H=2, data=0),
                     T(B=0, S=1, H=8, data=0)) == A.ATTN_OK
+
+
+# --------------------------------------------------------------------------
+# attn_fwd_decode_noalloc: the same checks, and the fixed-workspace limit,
+# all rejected before any HIP call
+# --------------------------------------------------------------------------
+def call_dec_na(lib, q, k, v, out, lens=None, causal=1, lse=None):
+    return lib.attn_fwd_decode_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), lens,
+                                       ctypes.c_float(0.0), causal, q.H, k.H, ctypes.byref(out), lse, None)
+
+
+def test_decode_noalloc_checks(lib):
+    q, k, v, o = T(S=1, H=8), T(S=100, H=2), T(S=100, H=2), T(S=1, H=8)
+    assert call_dec_na(lib, q, k, T(S=99, H=2), o) == A.ATTN_ERR_SHAPE
+    assert call_dec_na(lib, q, T(S=100, H=3), T(S=100, H=3), o) == A.ATTN_ERR_HEADS
+    assert call_dec_na(lib, q, k, v, o, causal=3) == A.ATTN_ERR_MASK
+    assert call_dec_na(lib, q, k, v, o, lens=FAKE + 2) == A.ATTN_ERR_ALIGN
+    assert call_dec_na(lib, T(S=1, H=8, data=0), k, v, o) == A.ATTN_ERR_NULL
+    assert call_dec_na(lib, T(S=0, H=8), k, v, T(S=0, H=8)) == A.ATTN_OK  # no row: nothing launched
+
+
+def test_decode_noalloc_rejects_sizes_beyond_its_workspace(lib):
+    limit = 32 << 20
+    # B=8, Hq=64, D=128, Sk=4096: 16 chunks x 512 rows x 131 floats = 4.3 MB, within the limit
+    assert A.decode_workspace_bytes(8, 1, 64, 128, 4096) <= limit
+    # 16 times the cache: 68.7 MB, beyond it
+    big = dict(B=8, H=8, D=128)
+    assert A.decode_workspace_bytes(8, 1, 64, 128, 65536) > limit
+    rc = call_dec_na(lib, T(S=1, B=8, H=64, D=128), T(S=65536, **big), T(S=65536, **big), T(S=1, B=8, H=64, D=128))
+    assert rc == A.ATTN_ERR_SCRATCH
+    assert "32 MiB" in A.strerror(rc)
 
 
 # --------------------------------------------------------------------------

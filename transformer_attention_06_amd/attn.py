@@ -27,11 +27,12 @@ ATTN_ERR_LAUNCH = -8
 ATTN_ERR_DEVICE = -9
 ATTN_ERR_ALIAS = -10
 ATTN_ERR_WORKSPACE = -11
+ATTN_ERR_SCRATCH = -12
 ATTN_MASK_ADDITIVE = 0
 ATTN_MASK_BOOL = 1
 
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_masked", "attn_fwd_rope", "attn_fwd_decode",
-                    "attn_decode_workspace_bytes", "attn_strerror", "attn_version")
+                    "attn_fwd_decode_noalloc", "attn_decode_workspace_bytes", "attn_strerror", "attn_version")
 
 
 class AttnTensor(ctypes.Structure):
@@ -78,6 +79,9 @@ def load_library(path=LIB_PATH):
                                     ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_void_p]
     lib.attn_fwd_decode.restype = ctypes.c_int
+    lib.attn_fwd_decode_noalloc.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, P, ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_fwd_decode_noalloc.restype = ctypes.c_int
     lib.attn_decode_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int64,
                                                 ctypes.c_int64]
     lib.attn_decode_workspace_bytes.restype = ctypes.c_int64
@@ -377,6 +381,39 @@ def attn_fwd_decode(q, k_cache, v_cache, cache_lens, scale, causal, n_q_heads, n
                                ctypes.c_void_p(workspace.data_ptr()),
                                ctypes.c_int64(workspace.numel() * workspace.element_size()),
                                ctypes.c_void_p(stream.cuda_stream))
+    check(code)
+    return out, lse
+
+
+def attn_fwd_decode_noalloc(q, k_cache, v_cache, cache_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
+                            stream=None):
+    """``attn_fwd_decode_noalloc`` with torch tensors (as attn_fwd_decode,
+    without a workspace).  Marshals only: nothing is allocated here or in the
+    library."""
+    import torch
+    lib = load_library()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    lens_ptr = None
+    if cache_lens is not None:
+        if cache_lens.dtype != torch.int32 or not cache_lens.is_cuda or not cache_lens.is_contiguous():
+            raise ValueError("cache_lens must be a contiguous int32 device tensor")
+        lens_ptr = ctypes.c_void_p(cache_lens.data_ptr())
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 device tensor")
+        if tuple(lse.shape) != (q.shape[0], n_q_heads, q.shape[1]):
+            raise ValueError("lse must be [B, n_q_heads, Sq]")
+        lse_ptr = ctypes.c_void_p(lse.data_ptr())
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    dq, dk, dv, do = describe(q), describe(k_cache), describe(v_cache), describe(out)
+    code = lib.attn_fwd_decode_noalloc(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), lens_ptr,
+                                       ctypes.c_float(0.0 if scale is None else float(scale)), int(bool(causal)),
+                                       int(n_q_heads), int(n_kv_heads), ctypes.byref(do), lse_ptr,
+                                       ctypes.c_void_p(stream.cuda_stream))
     check(code)
     return out, lse
 

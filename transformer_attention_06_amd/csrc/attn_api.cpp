@@ -242,10 +242,13 @@ extern "C" int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_he
     return n_split * rows * (D + 3) * int64_t(sizeof(float));
 }
 
-extern "C" int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_cache,
-                               const attn_tensor_t* v_cache, const int32_t* cache_lens, float scale,
-                               int causal, int n_q_heads, int n_kv_heads, const attn_tensor_t* out,
-                               float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+// Argument checks and launch parameters shared by the two decode entry
+// points (no HIP call).  *need receives the workspace bytes; a returned
+// ATTN_OK with a->B == 0 or a->Sq == 0 means there is nothing to launch.
+static int decode_prepare(const attn_tensor_t* q, const attn_tensor_t* k_cache, const attn_tensor_t* v_cache,
+                          const int32_t* cache_lens, float scale, int causal, int n_q_heads, int n_kv_heads,
+                          const attn_tensor_t* out, float* lse, void* stream, attn_detail::DecodeArgs* a,
+                          int64_t* need) {
     if (!q || !k_cache || !v_cache || !out) return ATTN_ERR_NULL;
     const attn_tensor_t* all[4] = {q, k_cache, v_cache, out};
     for (const attn_tensor_t* t : all)
@@ -266,42 +269,74 @@ extern "C" int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_ca
     if (cache_lens && (reinterpret_cast<uintptr_t>(cache_lens) & 3u) != 0) return ATTN_ERR_ALIGN;
     if (q->D != 64 && q->D != 128) return ATTN_ERR_UNSUPPORTED;
     const int64_t B = q->B, Sq = q->S, Sk = k_cache->S, D = q->D;
+    a->B = B;
+    a->Sq = Sq;
+    *need = 0;
     if (B == 0 || Sq == 0) return ATTN_OK;  // no query row: nothing to launch
     if (Sk >= (int64_t(1) << 29) || Sq >= (int64_t(1) << 20)) return ATTN_ERR_UNSUPPORTED;
     if (B > 65535 || B * n_kv_heads > 65535) return ATTN_ERR_UNSUPPORTED;
     const int64_t rows_per_kv = int64_t(n_q_heads / n_kv_heads) * Sq;
     if ((rows_per_kv + 7) / 8 > 65535) return ATTN_ERR_UNSUPPORTED;
     if (B * n_q_heads * Sq / 4 + 1 >= int64_t(1) << 31) return ATTN_ERR_UNSUPPORTED;
-    const int64_t need = attn_decode_workspace_bytes(B, Sq, n_q_heads, D, Sk);
+    *need = attn_decode_workspace_bytes(B, Sq, n_q_heads, D, Sk);
     if (!q->data || !out->data) return ATTN_ERR_NULL;
     if (Sk > 0 && (!k_cache->data || !v_cache->data)) return ATTN_ERR_NULL;
-    if (!workspace) return ATTN_ERR_NULL;
-    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    if (!aligned16(q->data) || !aligned16(out->data) || !aligned16(workspace) ||
+    if (!aligned16(q->data) || !aligned16(out->data) ||
         (Sk > 0 && (!aligned16(k_cache->data) || !aligned16(v_cache->data))))
         return ATTN_ERR_ALIGN;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return ATTN_ERR_ALIGN;
     float sc = scale;
     if (!(sc > 0.0f) || !std::isfinite(sc)) sc = 1.0f / std::sqrt(float(D));
+    a->q = q->data;
+    a->k = k_cache->data;
+    a->v = v_cache->data;
+    a->o = out->data;
+    a->lse = lse;
+    a->cache_lens = cache_lens;
+    a->workspace = nullptr;
+    a->dtype = q->dtype;
+    a->Sk = Sk;
+    a->Hq = n_q_heads;
+    a->Hkv = n_kv_heads;
+    a->D = D;
+    a->causal = causal;
+    a->n_split = attn_detail::decode_splits(Sk);
+    a->scale = sc;
+    a->stream = stream;
+    return ATTN_OK;
+}
+
+extern "C" int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_cache,
+                               const attn_tensor_t* v_cache, const int32_t* cache_lens, float scale,
+                               int causal, int n_q_heads, int n_kv_heads, const attn_tensor_t* out,
+                               float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
     attn_detail::DecodeArgs a;
-    a.q = q->data;
-    a.k = k_cache->data;
-    a.v = v_cache->data;
-    a.o = out->data;
-    a.lse = lse;
-    a.cache_lens = cache_lens;
+    int64_t need = 0;
+    const int rc = decode_prepare(q, k_cache, v_cache, cache_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
+                                  stream, &a, &need);
+    if (rc != ATTN_OK || a.B == 0 || a.Sq == 0) return rc;
+    if (!workspace) return ATTN_ERR_NULL;
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
     a.workspace = workspace;
-    a.dtype = q->dtype;
-    a.B = B;
-    a.Sq = Sq;
-    a.Sk = Sk;
-    a.Hq = n_q_heads;
-    a.Hkv = n_kv_heads;
-    a.D = D;
-    a.causal = causal;
-    a.n_split = attn_detail::decode_splits(Sk);
-    a.scale = sc;
-    a.stream = stream;
+    return attn_detail::launch_decode(a);
+}
+
+// The same decode without any allocation: the workspace is the library's
+// fixed per-GPU array (attn_detail::decode_scratch).  Checks first, then the
+// size limit, then the one-time address lookup, then the two launches.
+extern "C" int attn_fwd_decode_noalloc(const attn_tensor_t* q, const attn_tensor_t* k_cache,
+                                       const attn_tensor_t* v_cache, const int32_t* cache_lens, float scale,
+                                       int causal, int n_q_heads, int n_kv_heads, const attn_tensor_t* out,
+                                       float* lse, void* stream) {
+    attn_detail::DecodeArgs a;
+    int64_t need = 0;
+    int rc = decode_prepare(q, k_cache, v_cache, cache_lens, scale, causal, n_q_heads, n_kv_heads, out, lse, stream,
+                            &a, &need);
+    if (rc != ATTN_OK || a.B == 0 || a.Sq == 0) return rc;
+    if (need > attn_detail::kDecodeScratchBytes) return ATTN_ERR_SCRATCH;
+    rc = attn_detail::decode_scratch(&a.workspace);
+    if (rc != ATTN_OK) return rc;
     return attn_detail::launch_decode(a);
 }
 
@@ -319,6 +354,7 @@ extern "C" const char* attn_strerror(int code) {
         case ATTN_ERR_DEVICE: return "the current device cannot run this library's gfx950 code";
         case ATTN_ERR_ALIAS: return "k_rot overlaps q, v, out, lse, or part of k (it may be k itself)";
         case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_decode_workspace_bytes() requires";
+        case ATTN_ERR_SCRATCH: return "attn_fwd_decode_noalloc: these sizes need more workspace than its fixed 32 MiB per GPU (attn_decode_workspace_bytes() > 33554432); use attn_fwd_decode with a caller workspace";
         default: return "unknown error code";
     }
 }

@@ -36,6 +36,8 @@
 // the time the cache bytes take at full HBM bandwidth.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include <cmath>
 #include <cstdint>
 
@@ -679,7 +681,30 @@ int launch_decode_dtype(const attn_detail::DecodeArgs& a) {
 
 }  // namespace
 
+// Workspace of the allocation-free entry point (attn_fwd_decode_noalloc): a
+// fixed device array, one copy per GPU for the life of the process.  In host
+// code the name below is a host-side stand-in, never a device address: the
+// device address is looked up with hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float attn_decode_scratch[attn_detail::kDecodeScratchBytes / sizeof(float)];
+
 namespace attn_detail {
+
+int decode_scratch(void** ws) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> addr[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_DEVICE;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // with this device current: its copy of the array (two threads that
+        // race here store the same address)
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(attn_decode_scratch)) != hipSuccess || p == nullptr)
+            return ATTN_ERR_DEVICE;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ws = p;
+    return ATTN_OK;
+}
 
 int decode_splits(int64_t Sk) { return Sk > kDecChunk ? int((Sk + kDecChunk - 1) / kDecChunk) : 1; }
 

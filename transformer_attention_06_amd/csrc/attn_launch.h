@@ -73,6 +73,14 @@ struct DecodeArgs {
 // Key chunks a cache of Sk rows is split into.
 int decode_splits(int64_t Sk);
 
+// Size of the fixed device workspace of the allocation-free decode entry
+// point (one array per GPU, shared by every call on that GPU).
+constexpr int64_t kDecodeScratchBytes = int64_t(32) << 20;
+
+// This device's address of that workspace (looked up on the first call on
+// each device); ATTN_OK or ATTN_ERR_DEVICE.
+int decode_scratch(void** ws);
+
 // Enqueue the split and merge kernels.
 int launch_decode(const DecodeArgs& a);
 
