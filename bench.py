@@ -166,6 +166,20 @@ def measured_traffic(name):
     return t.get("traffic_bytes_per_launch")
 
 
+def measured_counters(name):
+    """The derived counter figures of a committed summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"counters_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    keys = ("shader_clock_ghz", "mfma_busy_pct", "valu_insts_per_mfma", "lds_insts_per_mfma",
+            "lds_bank_conflict_pct", "wave_waiting_pct", "ta_busy_pct")
+    return {k: round(c[k], 4) for k in keys} | {"source": f"profiles/counters_{name}.json"}
+
+
 def copy_calibration(nbytes=1 << 29, reps=3):
     """A plain device-to-device copy of known size, for scaling the memory
     traffic counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
@@ -179,37 +193,153 @@ def copy_calibration(nbytes=1 << 29, reps=3):
                       "kernel_source_sha": kernel_source_sha()}), flush=True)
 
 
-def write_traffic(prof_dir, name=DEFAULT_WORKLOAD):
-    """Write profiles/traffic_<name>.json from four rocprofv3 --pmc runs under
-    prof_dir (fetch_c2, write_c2: the benchmark; fetch_copy, write_copy: the
-    512 MiB copy calibration), each holding p_counter_collection.csv: the
-    attention kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-    scaled by what the counter reads for the copy of known size."""
+def _counter_rows(prof_dir, sub, kernel):
+    """Rows of prof_dir/sub/p_counter_collection.csv (one rocprofv3 --pmc
+    run) for dispatches of `kernel`, grouped per dispatch: {id: {"name",
+    "dur_ns", counter: value summed over the counter's dimensions}}."""
     import csv
+    path = os.path.join(prof_dir, sub, "p_counter_collection.csv")
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if kernel not in r["Kernel_Name"]:
+            continue
+        d = out.setdefault(int(r["Dispatch_Id"]), {"dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _pmc_cmd(counters, prof_dir, sub, args):
+    return f"rocprofv3 --pmc {counters} --output-format csv -d {prof_dir}/{sub} -o p -- python3 bench.py {args}"
+
+
+def write_traffic(prof_dir, name=DEFAULT_WORKLOAD, out_dir=None):
+    """Write profiles/traffic_<name>.json from four rocprofv3 --pmc runs under
+    prof_dir (fetch_<name>, write_<name>: the workload; fetch_copy,
+    write_copy: the 512 MiB copy calibration), each holding
+    p_counter_collection.csv: the attention kernel's FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for
+    the copy of known size."""
     import statistics
 
-    def values(sub, kernel):
-        path = os.path.join(prof_dir, sub, "p_counter_collection.csv")
-        return [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]]
+    def values(sub, kernel, counter):
+        return [d[counter] for d in _counter_rows(prof_dir, sub, kernel).values() if counter in d]
 
     nbytes_kib = (1 << 29) / 1024.0
-    fetch, write = values("fetch_c2", "attn_fwd_kernel"), values("write_c2", "attn_fwd_kernel")
-    fscale = nbytes_kib / statistics.median(values("fetch_copy", "copyBuffer"))
-    wscale = nbytes_kib / statistics.median(values("write_copy", "copyBuffer"))
+    fetch = values(f"fetch_{name}", "attn_fwd_kernel", "FETCH_SIZE")
+    write = values(f"write_{name}", "attn_fwd_kernel", "WRITE_SIZE")
+    fscale = nbytes_kib / statistics.median(values("fetch_copy", "copyBuffer", "FETCH_SIZE"))
+    wscale = nbytes_kib / statistics.median(values("write_copy", "copyBuffer", "WRITE_SIZE"))
     fk, wk = statistics.mean(fetch), statistics.mean(write)
-    cmd = "rocprofv3 --pmc {c} --output-format csv -d {d}/{sub} -o p -- python3 bench.py {args}"
+    run = f"--workload {name} --steps 5 --warmup 2 --no-cpu-baseline"
     out = {"workload": name, "kernel_source_sha": kernel_source_sha(),
            "fetch_size_kib_per_dispatch": fk, "write_size_kib_per_dispatch": wk,
            "fetch_scale": fscale, "write_scale": wscale,
            "traffic_bytes_per_launch": (fk * fscale + wk * wscale) * 1024.0,
-           "commands": [cmd.format(c=c, d=prof_dir, sub=sub, args=args) for c, sub, args in (
-               ("FETCH_SIZE", "fetch_c2", "--steps 5 --warmup 2 --no-cpu-baseline"),
-               ("WRITE_SIZE", "write_c2", "--steps 5 --warmup 2 --no-cpu-baseline"),
+           "commands": [_pmc_cmd(c, prof_dir, sub, args) for c, sub, args in (
+               ("FETCH_SIZE", f"fetch_{name}", run),
+               ("WRITE_SIZE", f"write_{name}", run),
                ("FETCH_SIZE", "fetch_copy", "--copy-calibration"),
                ("WRITE_SIZE", "write_copy", "--copy-calibration"))]}
-    with open(os.path.join(ROOT, "profiles", f"traffic_{name}.json"), "w") as f:
+    with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{name}.json"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out), flush=True)
+
+
+# Two counter passes per workload (rocprofv3 collects at most 8 SQ, 2 TA and
+# 2 GRBM counters per run).  SQ counters are summed over the 32 shader
+# engines (4 per XCD), GRBM_GUI_ACTIVE over the 8 XCDs: one XCD's busy
+# cycles are GRBM_GUI_ACTIVE / 8, and that over the dispatch's duration is
+# the shader clock.  SQ_VALU_MFMA_BUSY_CYCLES sums the matrix-core busy
+# cycles of all 1024 SIMDs, so MFMA busy = it / (1024 x one XCD's cycles).
+# The SQ_WAVE_CYCLES / SQ_WAIT_ANY / SQ_ACTIVE_INST_* family counts wave
+# cycles in one common unit; only their ratios are used.
+PMC_PASSES = {
+    "pmc_sq": "SQ_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_{mops} SQ_INSTS_MFMA SQ_INSTS_VALU "
+              "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE",
+    "pmc_wait": "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+                "SQ_ACTIVE_INST_VMEM SQ_VALU_MFMA_COEXEC_CYCLES SQ_INST_CYCLES_VMEM_RD TA_TA_BUSY GRBM_GUI_ACTIVE",
+}
+N_XCD, N_SIMD, N_CU = 8, 1024, 256
+
+
+def write_counters(prof_dir, name=DEFAULT_WORKLOAD, out_dir=None):
+    """Write profiles/counters_<name>.json and profiles/attn_fwd_<name>_counters.md
+    from the two rocprofv3 --pmc passes under prof_dir (pmc_sq_<name>,
+    pmc_wait_<name>, each a run of bench.py on the workload)."""
+    import statistics
+    from transformer_attention_06_amd import workloads as W
+    w = W.WORKLOADS[name]
+    mops = {"bf16": "BF16", "fp16": "F16", "fp32": "F32"}[w.dtype]
+    a = _counter_rows(prof_dir, f"pmc_sq_{name}", "attn_fwd_kernel")
+    b = _counter_rows(prof_dir, f"pmc_wait_{name}", "attn_fwd_kernel")
+    m = lambda rows, f: statistics.mean(f(d) for d in rows.values())
+    cyc_a = lambda d: d["GRBM_GUI_ACTIVE"] / N_XCD
+    cyc_b = lambda d: d["GRBM_GUI_ACTIVE"] / N_XCD
+    mfma_flops = m(a, lambda d: d[f"SQ_INSTS_VALU_MFMA_MOPS_{mops}"] * 512.0)
+    c = {
+        "workload": name, "kernel_source_sha": kernel_source_sha(), "dispatches": [len(a), len(b)],
+        "dispatch_us_mean": m(a, lambda d: d["dur_ns"] / 1e3),
+        "xcd_cycles_mean": m(a, cyc_a),
+        "shader_clock_ghz": m(a, lambda d: cyc_a(d) / d["dur_ns"]),
+        "sq_cycles_per_se_over_xcd_cycles": m(a, lambda d: d["SQ_CYCLES"] / 32 / cyc_a(d)),
+        "mfma_busy_pct": 100.0 * m(a, lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * cyc_a(d))),
+        "mfma_flops_per_dispatch": mfma_flops,
+        "mfma_flops_over_metric_flops": mfma_flops / metric_flops(w),
+        "valu_insts_per_mfma": m(a, lambda d: d["SQ_INSTS_VALU"] / d["SQ_INSTS_MFMA"]),
+        "lds_insts_per_mfma": m(a, lambda d: d["SQ_INSTS_LDS"] / d["SQ_INSTS_MFMA"]),
+        "lds_bank_conflict_pct": 100.0 * m(a, lambda d: d["SQ_LDS_BANK_CONFLICT"] / max(d["SQ_LDS_IDX_ACTIVE"], 1.0)),
+        "wave_waiting_pct": 100.0 * m(b, lambda d: d["SQ_WAIT_ANY"] / d["SQ_WAVE_CYCLES"]),
+        "wave_issuing_pct": 100.0 * m(b, lambda d: d["SQ_ACTIVE_INST_ANY"] / d["SQ_WAVE_CYCLES"]),
+        "wave_valu_pct": 100.0 * m(b, lambda d: d["SQ_ACTIVE_INST_VALU"] / d["SQ_WAVE_CYCLES"]),
+        "wave_lds_pct": 100.0 * m(b, lambda d: d["SQ_ACTIVE_INST_LDS"] / d["SQ_WAVE_CYCLES"]),
+        "wave_vmem_pct": 100.0 * m(b, lambda d: d["SQ_ACTIVE_INST_VMEM"] / d["SQ_WAVE_CYCLES"]),
+        "mfma_coexec_over_mfma_busy": m(b, lambda d: d["SQ_VALU_MFMA_COEXEC_CYCLES"] / N_SIMD / cyc_b(d)) /
+                                      max(m(a, lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cyc_a(d)), 1e-9),
+        "ta_busy_pct": 100.0 * m(b, lambda d: d["TA_TA_BUSY"] / (N_CU * cyc_b(d))),
+        "commands": [_pmc_cmd(PMC_PASSES[p].format(mops=mops), prof_dir, f"{p}_{name}",
+                              f"--workload {name} --steps 5 --warmup 2 --no-cpu-baseline") for p in PMC_PASSES],
+    }
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    with open(os.path.join(out_dir, f"counters_{name}.json"), "w") as f:
+        json.dump(c, f, indent=1)
+    rows = [
+        ("dispatches (pass 1, pass 2)", f"{c['dispatches'][0]}, {c['dispatches'][1]}"),
+        ("dispatch duration under counters (µs, mean)", f"{c['dispatch_us_mean']:.2f}"),
+        ("busy cycles of one XCD (GRBM_GUI_ACTIVE / 8)", f"{c['xcd_cycles_mean']:.4g}"),
+        ("shader clock (XCD cycles / duration, GHz)", f"{c['shader_clock_ghz']:.3f}"),
+        ("SQ_CYCLES / 32 shader engines ÷ XCD cycles (consistency)", f"{c['sq_cycles_per_se_over_xcd_cycles']:.3f}"),
+        ("MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs × XCD cycles))", f"{c['mfma_busy_pct']:.1f} %"),
+        ("MFMA FLOPs / metric FLOPs", f"{c['mfma_flops_over_metric_flops']:.4f}"),
+        ("VALU instructions (incl. MFMA) per MFMA", f"{c['valu_insts_per_mfma']:.2f}"),
+        ("LDS instructions per MFMA", f"{c['lds_insts_per_mfma']:.2f}"),
+        ("LDS bank conflicts (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)", f"{c['lds_bank_conflict_pct']:.2f} %"),
+        ("wave cycles waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES)", f"{c['wave_waiting_pct']:.1f} %"),
+        ("wave cycles issuing any instruction (SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES)", f"{c['wave_issuing_pct']:.1f} %"),
+        ("  VALU / LDS / VMEM issue (SQ_ACTIVE_INST_* / SQ_WAVE_CYCLES)",
+         f"{c['wave_valu_pct']:.1f} / {c['wave_lds_pct']:.1f} / {c['wave_vmem_pct']:.1f} %"),
+        ("MFMA cycles with VALU co-issued (SQ_VALU_MFMA_COEXEC_CYCLES / MFMA busy)",
+         f"{c['mfma_coexec_over_mfma_busy']:.2f}"),
+        ("TA busy (TA_TA_BUSY / (256 CUs × XCD cycles))", f"{c['ta_busy_pct']:.1f} %"),
+    ]
+    md = [f"# attn_fwd hardware counters — {name}", "",
+          f"Workload: {w.name} (B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} {w.dtype}"
+          f"{' causal' if w.causal else ''}{' key-padding' if w.mask_kind else ''}{' LSE' if w.want_lse else ''}).",
+          f"Kernel source sha256[:16]: `{c['kernel_source_sha']}`.", "",
+          "Two rocprofv3 counter passes, run from the repository root:", ""]
+    md += [f"- `{cmd}`" for cmd in c["commands"]]
+    md += ["", f"Summary written by `python3 bench.py --write-counters {prof_dir} --workload {name}`; values are means "
+           "over the attention kernel's dispatches.", "",
+           "Normalisation: SQ counters are summed over the 32 shader engines (4 per XCD) and GRBM_GUI_ACTIVE over "
+           "the 8 XCDs, so one XCD's busy cycles are GRBM_GUI_ACTIVE / 8 (SQ_CYCLES / 32 agrees, row 5); those "
+           "cycles over the dispatch's duration are the shader clock. SQ_VALU_MFMA_BUSY_CYCLES sums the matrix-core "
+           "busy cycles of all 1024 SIMDs (it equals 32 cycles × MFMA instructions here), hence MFMA busy = "
+           "SQ_VALU_MFMA_BUSY_CYCLES / (1024 × XCD cycles). The wave-state counters (SQ_WAVE_CYCLES, SQ_WAIT_ANY, "
+           "SQ_ACTIVE_INST_*) share one unit and are used only as ratios.", "",
+           "| quantity | value |", "|---|---|"]
+    md += [f"| {k} | {v} |" for k, v in rows]
+    with open(os.path.join(out_dir, f"attn_fwd_{name}_counters.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(c), flush=True)
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -452,6 +582,7 @@ def bench_one(name, steps, warmup, with_cpu, use_graph=True, warmup_s=0.0, rope=
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name),
+                     "counters": measured_counters(w.name),
                      "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 3),
                      "flops_per_launch": fl,
                      "min_hbm_bytes_per_launch": min_hbm_bytes(w, r["pad"]),
@@ -502,6 +633,9 @@ def main():
     ap.add_argument("--write-traffic", metavar="PROF_DIR",
                     help="write profiles/traffic_<workload>.json from the four rocprofv3 --pmc runs under PROF_DIR "
                          "(no GPU needed)")
+    ap.add_argument("--write-counters", metavar="PROF_DIR",
+                    help="write profiles/counters_<workload>.json and its .md summary from the two rocprofv3 --pmc "
+                         "passes under PROF_DIR (no GPU needed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 512 MiB device copy (counter calibration) and exit")
     ap.add_argument("--decode", action="store_true",
@@ -523,7 +657,10 @@ def main():
     if args.warmup is None:
         args.warmup = 20
     if args.write_traffic:
-        write_traffic(args.write_traffic)
+        write_traffic(args.write_traffic, args.workload)
+        return
+    if args.write_counters:
+        write_counters(args.write_counters, args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -304,7 +304,7 @@ int attn_fwd_decode_noalloc(const attn_tensor_t* q, const attn_tensor_t* k_cache
 
 /* Bytes of workspace attn_fwd_decode needs for these sizes: one 256-key chunk
  * (at least one, also for an empty cache) × B·Hq·Sq rows × (D + 3) floats;
- * -1 if a size is negative. */
+ * -1 if a size is negative or the count does not fit in int64. */
 int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_heads, int64_t D, int64_t Sk);
 
 /* Static, human-readable text for a return code (never NULL). */

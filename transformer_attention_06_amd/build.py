@@ -17,9 +17,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn_fwd.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", "attn_decode_kernels.hip", "attn_masked_kernels.hip"]
 # kernels whose MFMAs are inline assembly: their device assembly is checked
-ASM_CHECKED = ["attn_fwd_kernels.hip"]
+ASM_CHECKED = [f"attn_fwd_{t}_d{d}.hip" for t in ("bf16", "f16", "f32") for d in (64, 128)]
+SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", *ASM_CHECKED, "attn_decode_kernels.hip",
+           "attn_masked_kernels.hip"]
 
 
 def source_hash():
@@ -58,20 +59,22 @@ def build(verbose=False, extra_flags=()):
     common = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
               f'-DATTN_SRC_HASH="{source_hash()}"', *DEVICE_FLAGS, *extra_flags]
     with tempfile.TemporaryDirectory() as td:
-        objs, procs = [], []
+        objs, procs, asms = [], [], []
         for src in SOURCES:
-            obj = os.path.join(td, os.path.splitext(src)[0] + ".o")
+            stem = os.path.splitext(src)[0]
+            obj = os.path.join(td, stem + ".o")
             objs.append(obj)
             cmd = [hipcc(), *common, "-c", "-Wall", "-Wno-unused-result", "-Wno-pass-failed", "-o", obj,
                    os.path.join(CSRC, src)]
-            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
-        asms = []
-        for src in ASM_CHECKED:
-            asm = os.path.join(td, os.path.splitext(src)[0] + ".s")
-            asms.append(asm)
-            acmd = [hipcc(), *common, "--cuda-device-only", "-S", "-Wno-pass-failed", "-o", asm,
-                    os.path.join(CSRC, src)]
-            procs.append((acmd, subprocess.Popen(acmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+            cwd = None
+            if src in ASM_CHECKED:
+                # one compilation that also leaves the device assembly behind
+                cwd = os.path.join(td, stem)
+                os.mkdir(cwd)
+                cmd.insert(-3, "-save-temps")
+                asms.append(os.path.join(cwd, f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}.s"))
+            procs.append((cmd, subprocess.Popen(cmd, cwd=cwd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                text=True)))
         for cmd, pr in procs:
             out, err = pr.communicate()
             if verbose:

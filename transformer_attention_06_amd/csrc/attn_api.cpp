@@ -11,6 +11,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 namespace {
 
@@ -237,9 +238,13 @@ extern "C" int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, con
 // transformer和ATB…" passes the cache into FlashAttention every step).
 extern "C" int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_heads, int64_t D, int64_t Sk) {
     if (B < 0 || Sq < 0 || n_q_heads < 0 || D < 0 || Sk < 0) return -1;
-    const int64_t rows = B * int64_t(n_q_heads) * Sq;
-    const int64_t n_split = attn_detail::decode_splits(Sk);
-    return n_split * rows * (D + 3) * int64_t(sizeof(float));
+    // n_split · B · Hq · Sq · 4 · (D + 3), or -1 where it does not fit int64
+    int64_t r = attn_detail::decode_splits(Sk);
+    for (int64_t x : {B, int64_t(n_q_heads), Sq, int64_t(sizeof(float))})
+        if (__builtin_mul_overflow(r, x, &r)) return -1;
+    int64_t d3 = 0;
+    if (__builtin_add_overflow(D, int64_t(3), &d3) || __builtin_mul_overflow(r, d3, &r)) return -1;
+    return r;
 }
 
 // Argument checks and launch parameters shared by the two decode entry
@@ -279,6 +284,7 @@ static int decode_prepare(const attn_tensor_t* q, const attn_tensor_t* k_cache, 
     if ((rows_per_kv + 7) / 8 > 65535) return ATTN_ERR_UNSUPPORTED;
     if (B * n_q_heads * Sq / 4 + 1 >= int64_t(1) << 31) return ATTN_ERR_UNSUPPORTED;
     *need = attn_decode_workspace_bytes(B, Sq, n_q_heads, D, Sk);
+    if (*need < 0) return ATTN_ERR_UNSUPPORTED;  // the workspace size does not fit int64
     if (!q->data || !out->data) return ATTN_ERR_NULL;
     if (Sk > 0 && (!k_cache->data || !v_cache->data)) return ATTN_ERR_NULL;
     if (!aligned16(q->data) || !aligned16(out->data) ||
@@ -300,7 +306,7 @@ static int decode_prepare(const attn_tensor_t* q, const attn_tensor_t* k_cache, 
     a->Hkv = n_kv_heads;
     a->D = D;
     a->causal = causal;
-    a->n_split = attn_detail::decode_splits(Sk);
+    a->n_split = int(attn_detail::decode_splits(Sk));  // Sk < 2^29: fits
     a->scale = sc;
     a->stream = stream;
     return ATTN_OK;

@@ -643,10 +643,16 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
     dp.causal = a.causal;
     if constexpr (sizeof(T) == 2) {
         const int n_rg = (dp.R + kDecRowsMfma - 1) / kDecRowsMfma;
+        attn_detail::log_launch("decode_mfma_kernel<%s, D=%d> grid=(%d, %lld, %d) block=%d Sk=%lld Sq=%lld",
+                                attn_detail::dtype_name(a.dtype), D, a.n_split, (long long)(a.B * a.Hkv), n_rg,
+                                kDecThreads, (long long)a.Sk, (long long)a.Sq);
         hipLaunchKernelGGL((decode_mfma_kernel<T, D>), dim3(unsigned(a.n_split), unsigned(a.B * a.Hkv), unsigned(n_rg)),
                            dim3(kDecThreads), 0, static_cast<hipStream_t>(a.stream), dp);
     } else {
         const int n_rg = (dp.R + kDecRows - 1) / kDecRows;
+        attn_detail::log_launch("decode_split_kernel<%s, D=%d> grid=(%d, %lld, %d) block=%d Sk=%lld Sq=%lld",
+                                attn_detail::dtype_name(a.dtype), D, a.n_split, (long long)(a.B * a.Hkv), n_rg,
+                                kDecThreads, (long long)a.Sk, (long long)a.Sq);
         hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(unsigned(a.n_split), unsigned(a.B * a.Hkv), unsigned(n_rg)),
                            dim3(kDecThreads), 0, static_cast<hipStream_t>(a.stream), dp);
     }
@@ -665,6 +671,8 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
         mp.Hq = dp.Hq;
         mp.n_split = dp.n_split;
         const int64_t blocks = (rows + 3) / 4;
+        attn_detail::log_launch("decode_merge_kernel<%s, D=%d> grid=%lld block=256 splits=%d",
+                                attn_detail::dtype_name(a.dtype), D, (long long)blocks, mp.n_split);
         hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(unsigned(blocks)), dim3(256), 0,
                            static_cast<hipStream_t>(a.stream), mp);
         e = hipGetLastError();
@@ -706,7 +714,7 @@ int decode_scratch(void** ws) {
     return ATTN_OK;
 }
 
-int decode_splits(int64_t Sk) { return Sk > kDecChunk ? int((Sk + kDecChunk - 1) / kDecChunk) : 1; }
+int64_t decode_splits(int64_t Sk) { return Sk > kDecChunk ? Sk / kDecChunk + (Sk % kDecChunk != 0) : 1; }
 
 int launch_decode(const DecodeArgs& a) {
     switch (a.dtype) {

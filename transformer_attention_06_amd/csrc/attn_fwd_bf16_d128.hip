@@ -1,0 +1,10 @@
+// attn_fwd_bf16_d128.hip — the __bf16, D = 128 instances of the fused attention
+// forward kernel (attn_fwd_kernel.h); one translation unit per element type
+// and head dim, so the instances compile in parallel.
+#include "attn_fwd_kernel.h"
+
+namespace attn_detail {
+
+int launch_fwd_bf16_d128(const LaunchArgs& a) { return launch_d<__bf16, 128>(a); }
+
+}  // namespace attn_detail

@@ -2,9 +2,36 @@
 // kernel launcher (not part of the public ABI).
 #pragma once
 
+#include <cstdarg>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 
 namespace attn_detail {
+
+// ATTN_LOG set to a value other than "" or "0": every launch prints one line
+// on stderr naming its kernel variant (template arguments), grid and
+// workgroup size, before the launch.
+inline bool log_on() {
+    static const bool on = [] {
+        const char* e = std::getenv("ATTN_LOG");
+        return e && e[0] && !(e[0] == '0' && e[1] == 0);
+    }();
+    return on;
+}
+
+inline void log_launch(const char* fmt, ...) {
+    if (!log_on()) return;
+    va_list ap;
+    va_start(ap, fmt);
+    std::fputs("[attn] ", stderr);
+    std::vfprintf(stderr, fmt, ap);
+    std::fputc('\n', stderr);
+    va_end(ap);
+}
+
+// name of an attn_dtype_t value
+inline const char* dtype_name(int32_t dt) { return dt == 2 ? "bf16" : dt == 1 ? "fp16" : "fp32"; }
 
 // Query rows owned by one workgroup (4 wavefronts x 32 rows).
 constexpr int kBlockM = 128;
@@ -41,6 +68,13 @@ struct LaunchArgs {
 
 // Enqueue the kernel; returns ATTN_OK or ATTN_ERR_LAUNCH / ATTN_ERR_DEVICE.
 int launch(const LaunchArgs& a);
+// the same per element type and head dim (one translation unit each)
+int launch_fwd_bf16_d64(const LaunchArgs& a);
+int launch_fwd_bf16_d128(const LaunchArgs& a);
+int launch_fwd_f16_d64(const LaunchArgs& a);
+int launch_fwd_f16_d128(const LaunchArgs& a);
+int launch_fwd_f32_d64(const LaunchArgs& a);
+int launch_fwd_f32_d128(const LaunchArgs& a);
 
 // Enqueue the attention with an additive mask tensor (16-bit types only).
 int launch_masked(const LaunchArgs& a);
@@ -70,8 +104,9 @@ struct DecodeArgs {
     void* stream;
 };
 
-// Key chunks a cache of Sk rows is split into.
-int decode_splits(int64_t Sk);
+// Key chunks a cache of Sk rows is split into (at least one; defined for
+// every Sk >= 0 without overflow).
+int64_t decode_splits(int64_t Sk);
 
 // Size of the fixed device workspace of the allocation-free decode entry
 // point (one array per GPU, shared by every call on that GPU).

@@ -485,6 +485,10 @@ int launch_m(const attn_detail::LaunchArgs& a) {
     constexpr int NG = MGroups<DP>::value;
     mp.pair = CAUSAL && (NG == 2 || int64_t((mp.n_qb + 1) / 2) * a.Hq * a.B >= 512) ? 1 : 0;
     const unsigned n_x = unsigned(mp.pair ? (mp.n_qb + 1) / 2 : mp.n_qb);
+    attn_detail::log_launch("masked_kernel<%s, DP=%d, causal=%d, mask_mode=%d, exact=%d> groups=%d grid=(%u, %lld, %lld) "
+                            "block=%d pair=%d D=%lld S=%lld",
+                            attn_detail::dtype_name(a.dtype), DP, int(CAUSAL), MK, int(EXACT), NG, n_x, (long long)a.Hq,
+                            (long long)a.B, kMThreads * NG, mp.pair, (long long)a.D, (long long)a.S);
     hipLaunchKernelGGL((masked_kernel<T, DP, CAUSAL, MK, EXACT>), dim3(n_x, unsigned(a.Hq), unsigned(a.B)),
                        dim3(kMThreads * NG), 0, static_cast<hipStream_t>(a.stream), mp);
     const hipError_t e = hipGetLastError();
