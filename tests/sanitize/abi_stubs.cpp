@@ -57,6 +57,16 @@ int launch_masked(const LaunchArgs& a) {
     return ATTN_OK;
 }
 
+int launch_masked_tuned(const LaunchArgs& a) {
+    check(a);
+    if (!a.mask || a.dtype == ATTN_F32 || (a.D != 64 && a.D != 128)) fail("tuned mask kernel");
+    if ((a.S * (a.mask_bool ? 1 : 2)) % 16 != 0) fail("mask rows of 16-byte multiples");
+    stub::args = a;
+    stub::last = stub::LAUNCH_MASKED_TUNED;
+    ++stub::calls;
+    return ATTN_OK;
+}
+
 int launch_general(const LaunchArgs& a) {
     check(a);
     if (a.dtype == ATTN_F32 || a.B > 65535) fail("general kernel");

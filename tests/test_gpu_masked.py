@@ -58,6 +58,10 @@ CASES = [
     (4, 1, 129, 2, 1, 64, "bf16", True),
     (5, 3, 65, 3, 1, 128, "fp16", True),
     (6, 1, 1, 2, 2, 64, "bf16", False),
+    # rows of 16-byte multiples at D = 64 / 128: the tuned kernel
+    (7, 2, 264, 4, 2, 64, "fp16", True),
+    (8, 1, 320, 4, 1, 64, "bf16", False),
+    (9, 2, 136, 2, 2, 128, "fp16", False),
 ]
 
 
@@ -161,6 +165,9 @@ def test_masked_causal_paired_blocks(B, S, Hq, Hkv, D, dtype, mshape):
     (2, 203, 4, 4, 64, "fp16", False, 2),   # S % 8 != 0: byte loads
     (1, 129, 2, 1, 64, "bf16", True, 3),
     (2, 96, 4, 2, 80, "fp16", True, 1),     # general head dim
+    (2, 208, 4, 2, 128, "bf16", True, 0),   # S % 16 == 0: the tuned kernel
+    (1, 144, 2, 2, 64, "fp16", False, 3),
+    (3, 272, 4, 1, 64, "bf16", True, 1),
 ])
 def test_masked_bool(B, S, Hq, Hkv, D, dtype, causal, si):
     """A torch.bool mask (True: the key takes part), every broadcast shape,

@@ -185,6 +185,12 @@ extern "C" int attn_fwd_masked(const attn_tensor_t* q, const attn_tensor_t* k, c
     a.mask_b = mask_B != 1 ? 1 : 0;
     a.mask_h = mask_H != 1 ? 1 : 0;
     a.mask_bool = mask_type == ATTN_MASK_BOOL ? 1 : 0;
+    // the tuned kernel stages 16-byte chunks of mask rows (8 additive entries
+    // or 16 bytes) and addresses a mask plane with 32-bit offsets; other
+    // shapes and head dims take the general kernel
+    const int64_t me = a.mask_bool ? 1 : 2;
+    if ((a.D == 64 || a.D == 128) && (a.S * me) % 16 == 0 && a.S * a.S * me < (int64_t(1) << 31))
+        return attn_detail::launch_masked_tuned(a);
     return attn_detail::launch_masked(a);
 }
 

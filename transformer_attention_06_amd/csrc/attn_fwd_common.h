@@ -149,6 +149,12 @@ struct KParams {
     float sl2;                      // scale * log2(e)
     const int32_t* rope_pos;        // (B, S) positions, or null for 0..S-1
     double rope_r1;                 // rho = base^(-2/D): theta_{i+1} / theta_i
+    // explicit mask tensor (Bm, Hm, S, S): additive in the input type or one
+    // byte per entry; mask_b / mask_h are 1 when it has a batch / head
+    // dimension of B / Hq
+    const void* mask;
+    int mask_b, mask_h;
+    float inv_scale;                // 1 / scale: the additive mask in raw score units
 };
 
 // Rotary embedding: cos and sin of position × theta_i, from f = theta_i / 2π.
@@ -209,6 +215,30 @@ __device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t lds_byte, ui
                  :
                  : "s"(lds_byte), "v"(voff), "s"(rs)
                  : "memory");
+}
+
+// s_waitcnt vmcnt(n) for 0 <= n < 16 (n a constant after unrolling), also
+// a compiler barrier for memory operations: the direct global->LDS loads
+// are assembly the compiler does not track.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+        case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+    }
 }
 
 }  // namespace

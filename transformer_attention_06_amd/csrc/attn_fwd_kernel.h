@@ -84,7 +84,13 @@ struct Groups {
 // tiles are double-buffered in LDS; step j loads K tile j+2 and V tile j+1
 // (one 1 KiB direct load per wavefront every few MFMAs) and ends with a wait
 // for those loads and one workgroup barrier.
-template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE>
+// MK: 0 no mask tensor; 1 an additive mask tensor in T; 2 a boolean mask
+// tensor (one byte per entry, nonzero: the key takes part).  With a mask
+// tensor each wavefront stages the 32 x BN block of its own rows for the
+// next tile in an LDS region of its own (direct loads at the start of the
+// step, waited on by that wavefront alone), and adds it to (or selects)
+// the scores of that tile before their row maxima are taken.
+template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE, int MK = 0>
 __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn_fwd_kernel(KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
@@ -114,6 +120,19 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     // Per group: K tiles [NBUF][BN][D], then V tiles [NBUF][BN][D], slots
     // swizzled.
     __shared__ __attribute__((aligned(1024))) T lds[NG * 2 * NBUF * TILE_E];
+    // Mask tensor tiles: per wavefront 32 rows x BN entries in NML blocks of
+    // 1 KiB, block i holding keys [MKPL·i, MKPL·(i+1)) of all 32 rows (32
+    // bytes per row: two 16-byte chunks, swapped on rows 8..15 and 24..31
+    // so that the 16 (32) lanes of one LDS read pass hit distinct banks).
+    // Block i is one direct load, so the scores of key block i can be masked
+    // as soon as that load has landed.
+    static_assert(MK == 0 || sizeof(T) == 2, "mask tensors with 16-bit inputs only");
+    constexpr int ME = MK == 1 ? int(sizeof(T)) : 1;  // bytes per mask entry
+    constexpr int MWAVE_B = MK ? 32 * BN * ME : 0;    // one wavefront's rows of a tile
+    constexpr int NML = MWAVE_B / 1024;               // 1 KiB loads per wavefront per tile
+    constexpr int MKPL = 1024 / (32 * ME);            // keys per load
+    static_assert(MK == 0 || (NML * 1024 == MWAVE_B && MKPL * ME == 32), "mask tile split into 1 KiB loads");
+    __shared__ __attribute__((aligned(1024))) uint8_t mlds[MK ? NG * 4 * MWAVE_B : 16];
 
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
@@ -472,6 +491,70 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
                     if (kidx(16 * blk + i, 0) >= rel) s[blk][i] = -INFINITY;
         }
     };
+    // ---- mask tensor tiles (MK != 0) ------------------------------------------
+    // Plane (b', h') of the mask; a wavefront's block of tile t covers query
+    // rows wrow0 + [0, 32) and keys t·BN + [0, BN).  Its loads read through
+    // a buffer resource that ends at the end of the plane (rows past S read
+    // as zero; keys past S within a row are hidden by mask_tile anyway).
+    // The plane holds fewer than 2^31 bytes (checked on the host).
+    const uint64_t mplane = MK ? reinterpret_cast<uint64_t>(p.mask) +
+                                     (uint64_t(p.mask_b ? b : 0) * uint64_t(p.mask_h ? p.Hq : 1) +
+                                      uint64_t(p.mask_h ? hq : 0)) * uint64_t(S) * uint64_t(S) * uint64_t(ME)
+                               : 0;
+    const uint32_t mplane_b = MK ? uint32_t(S) * uint32_t(S) * uint32_t(ME) : 0;
+    const uint32_t mlds_w = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>(mlds)) + uint32_t(wave * MWAVE_B));
+    const uint8_t* const mrow = mlds + wave * MWAVE_B + r * 32;  // this lane's row in block 0
+    const int mhalf = (r >> 3) & 1;                                 // chunk swap of this lane's row
+    // the wavefront's block of mask tile t into its region: lane l of load i
+    // fills row l / 2, physical chunk l % 2
+    auto load_mask = [&](int t) __attribute__((always_inline)) {
+        if constexpr (MK != 0) {
+            const uint32_t off = (uint32_t(wrow0) * uint32_t(S) + uint32_t(t * BN)) * uint32_t(ME);
+            const uint64_t a = mplane + off;
+            const i32x4 rs{__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
+                           __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff)),
+                           __builtin_amdgcn_readfirstlane(int(off < mplane_b ? mplane_b - off : 0u)), 0x00020000};
+            const int row = lane >> 1;
+            const uint32_t voff = uint32_t(row) * uint32_t(S * ME) + uint32_t(((lane & 1) ^ ((row >> 3) & 1)) * 16);
+#pragma unroll
+            for (int i = 0; i < NML; ++i)
+                lds_dma16(rs, mlds_w + uint32_t(i * 1024), voff + uint32_t(i * MKPL * ME));
+        }
+    };
+    // the load that brings the entries of scores 8j..8j+7 (keys 16j + 8·gl
+    // + 0..7 of the lane's row), and those entries: 8 additive values (16
+    // bytes) or 8 bytes
+    auto mask_load_of = [](int j) __attribute__((always_inline)) { return 16 * j / MKPL; };
+    using mchunk_t = typename std::conditional<MK == 2, uint2, u32x4>::type;
+    auto read_mask = [&](int j) __attribute__((always_inline)) -> mchunk_t {
+        const uint8_t* blk = mrow + mask_load_of(j) * 1024;
+        if constexpr (MK == 2)
+            return *reinterpret_cast<const uint2*>(blk + (((j & 1) ^ mhalf) * 16) + 8 * gl);
+        else
+            return *reinterpret_cast<const u32x4*>(blk + ((gl ^ mhalf) * 16));
+    };
+    // scores f = 8j + [e0, e1) of s take their mask entries from chunk m
+    const float inv_scale = p.inv_scale;
+    auto apply_mask = [&](f32x16 (&s)[NBLK], const mchunk_t& m, int j, int e0, int e1)
+                          __attribute__((always_inline)) {
+        if constexpr (MK != 0) {
+#pragma unroll
+            for (int e = e0; e < e1; ++e) {
+                const int f = 8 * j + e;
+                const float x = s[f >> 4][f & 15];
+                if constexpr (MK == 2) {
+                    const uint32_t w = e < 4 ? m.x : m.y;
+                    s[f >> 4][f & 15] = ((w >> (8 * (e & 3))) & 0xffu) ? x : -INFINITY;
+                } else {
+                    const uint32_t w = m[e >> 1];
+                    const uint16_t h = uint16_t(e & 1 ? w >> 16 : w);
+                    s[f >> 4][f & 15] = fmaf(float(__builtin_bit_cast(T, h)), inv_scale, x);
+                }
+            }
+        }
+    };
+
     // Softmax work of one tile, split so it can ride along MFMAs:
     //   max_item(k): partial row maxima over scores 4k..4k+3 (four chains);
     //   fin0: the row max over both lane halves, scaled to log2 units;
@@ -573,6 +656,19 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     constexpr int NKA = (NKC + 1) / 2;     // P operands exponentiated in part A
     constexpr int NEA = NKA * KPL;         // their scores
     constexpr int MX0 = N2 / 8 > 1 ? N2 / 8 : 1;  // first part-B slot reading S(t+1)
+    // part-B slot that takes row-max item k of S(t+1)
+    constexpr auto mx_slot = [](int k) {
+        for (int i = MX0; i < N2; ++i)
+            if (k < (i - MX0 + 1) * NMX / (N2 - MX0)) return i;
+        return N2 - 1;
+    };
+    // mask tensor: the part-B slot that reads the entries of scores 8j..8j+7
+    // (two slots before their first row-max item), after waiting for the
+    // load that brought them; the NML mask loads of a step precede its 2·NLD
+    // tile loads, so load i has landed at vmcnt(2·NLD + NML - 1 - i)
+    constexpr auto mrd_slot = [mx_slot](int j) { return mx_slot(2 * j) >= 2 ? mx_slot(2 * j) - 2 : 0; };
+    auto mask_wait = [](int li) __attribute__((always_inline)) { wait_vmcnt(2 * NLD + NML - 1 - li); };
+    mchunk_t mk[2];
     op_t pb[NKC];
     // par: (t - first tile of the segment) % 2; K tile t+1 is in K buffer
     // 1 - par, V tile t in V buffer par, and this step loads K tile t+2 into
@@ -595,6 +691,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
 #pragma unroll
         for (int i = 0; i < N1; ++i) {
             if (G1) {
+                if (MK != 0 && i == 0) load_mask(t + 1);
                 if (i % (N1 / NL) == 0) load_one(t + KD, t + VD, par, 1 - par, i / (N1 / NL));
                 if (i + PF < N1 + N2) fetch(i + PF);
                 if (i < NBLK)
@@ -629,11 +726,21 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
                 }
             }
             if (G1) {
+                if constexpr (MK != 0) {
+#pragma unroll
+                    for (int mj = 0; mj < NF / 8; ++mj)
+                        if (i == mrd_slot(mj)) {
+                            mask_wait(mask_load_of(mj));
+                            mk[mj & 1] = read_mask(mj);
+                        }
+                }
                 if (i == MX0) mask_tile(sn, t + 1);
                 if (i >= MX0) {
 #pragma unroll
-                    for (int k = (i - MX0) * NMX / (N2 - MX0); k < (i - MX0 + 1) * NMX / (N2 - MX0); ++k)
+                    for (int k = (i - MX0) * NMX / (N2 - MX0); k < (i - MX0 + 1) * NMX / (N2 - MX0); ++k) {
+                        apply_mask(sn, mk[(k >> 1) & 1], k >> 1, 4 * (k & 1), 4 * (k & 1) + 4);
                         max_item(sn, k);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -675,6 +782,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             for (int k = 0; k < VD; ++k)
 #pragma unroll
                 for (int i = NLD; i < 2 * NLD; ++i) load_one(0, t0 + k, 0, k, i);
+            load_mask(t0);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles
             __syncthreads();
             ++n_bar;
@@ -701,6 +809,10 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             __syncthreads();
             ++n_bar;
             mask_tile(sa, t0);
+            if constexpr (MK != 0) {
+#pragma unroll
+                for (int mj = 0; mj < NF / 8; ++mj) apply_mask(sa, read_mask(mj), mj, 0, 8);
+            }
 #pragma unroll
             for (int k = 0; k < NMX; ++k) max_item(sa, k);
             fin0();
@@ -784,7 +896,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE>
+template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE, int MK = 0>
 int launch_t(const attn_detail::LaunchArgs& a) {
     KParams kp;
     kp.q = a.q;
@@ -807,15 +919,19 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     kp.rope_r1 = std::exp2(-2.0 * a.rope_lb / D);
     kp.cu = a.cu_seqlens;
     kp.total = int(a.total);
+    kp.mask = a.mask;
+    kp.mask_b = a.mask_b;
+    kp.mask_h = a.mask_h;
+    kp.inv_scale = 1.0f / a.scale;
     constexpr int NG = Groups<T, CAUSAL>::value;
     const int n_tasks = NG == 2 ? (kp.n_qb + 1) / 2 : kp.n_qb;
     const int64_t n_wg = int64_t(n_tasks) * kp.n_units;
-    attn_detail::log_launch("attn_fwd_kernel<%s, D=%d, causal=%d, pad=%d, lse=%d, rope=%d> groups=%d grid=%lld "
-                            "block=%d xcd_chunk=%d packed=%d B=%lld S=%lld Hq=%lld Hkv=%lld",
-                            attn_detail::dtype_name(a.dtype), D, int(CAUSAL), int(PAD), int(LSE), int(ROPE), NG,
+    attn_detail::log_launch("attn_fwd_kernel<%s, D=%d, causal=%d, pad=%d, lse=%d, rope=%d, mask=%d> groups=%d "
+                            "grid=%lld block=%d xcd_chunk=%d packed=%d B=%lld S=%lld Hq=%lld Hkv=%lld",
+                            attn_detail::dtype_name(a.dtype), D, int(CAUSAL), int(PAD), int(LSE), int(ROPE), MK, NG,
                             (long long)n_wg, kThreads * NG, kp.xcd_chunk, a.cu_seqlens ? 1 : 0, (long long)a.B,
                             (long long)a.S, (long long)a.Hq, (long long)a.Hkv);
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD, LSE, ROPE>), dim3(unsigned(n_wg)), dim3(kThreads * NG), 0,
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, CAUSAL, PAD, LSE, ROPE, MK>), dim3(unsigned(n_wg)), dim3(kThreads * NG), 0,
                        static_cast<hipStream_t>(a.stream), kp);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) return ATTN_OK;
@@ -832,6 +948,19 @@ int launch_r(const attn_detail::LaunchArgs& a) {
 template <typename T, int D, bool LSE>
 int launch_l(const attn_detail::LaunchArgs& a) {
     return a.rope ? launch_r<T, D, LSE, true>(a) : launch_r<T, D, LSE, false>(a);
+}
+
+// with a mask tensor (16-bit types; no key padding, no rotary embedding)
+template <typename T, int D, int MK>
+int launch_mask_k(const attn_detail::LaunchArgs& a) {
+    if (a.causal)
+        return a.lse ? launch_t<T, D, true, false, true, false, MK>(a) : launch_t<T, D, true, false, false, false, MK>(a);
+    return a.lse ? launch_t<T, D, false, false, true, false, MK>(a) : launch_t<T, D, false, false, false, false, MK>(a);
+}
+
+template <typename T, int D>
+int launch_mask_d(const attn_detail::LaunchArgs& a) {
+    return a.mask_bool ? launch_mask_k<T, D, 2>(a) : launch_mask_k<T, D, 1>(a);
 }
 
 template <typename T, int D>

@@ -117,6 +117,12 @@ int launch_rope_k(const LaunchArgs& a, void* k_out) {
     }
 }
 
+int launch_masked_tuned(const LaunchArgs& a) {
+    const bool d64 = a.D == 64;
+    if (a.dtype == ATTN_BF16) return d64 ? launch_fwd_mask_bf16_d64(a) : launch_fwd_mask_bf16_d128(a);
+    return d64 ? launch_fwd_mask_f16_d64(a) : launch_fwd_mask_f16_d128(a);
+}
+
 int launch(const LaunchArgs& a) {
     const bool d64 = a.D == 64;
     switch (a.dtype) {

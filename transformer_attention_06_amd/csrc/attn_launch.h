@@ -76,6 +76,14 @@ int launch_fwd_f16_d128(const LaunchArgs& a);
 int launch_fwd_f32_d64(const LaunchArgs& a);
 int launch_fwd_f32_d128(const LaunchArgs& a);
 
+// The tuned kernel with a mask tensor (a.mask; 16-bit types, D = 64 or 128,
+// rows of 16-byte multiples, planes under 2^31 bytes).
+int launch_masked_tuned(const LaunchArgs& a);
+int launch_fwd_mask_bf16_d64(const LaunchArgs& a);
+int launch_fwd_mask_bf16_d128(const LaunchArgs& a);
+int launch_fwd_mask_f16_d64(const LaunchArgs& a);
+int launch_fwd_mask_f16_d128(const LaunchArgs& a);
+
 // Enqueue the attention with an additive mask tensor (16-bit types only).
 int launch_masked(const LaunchArgs& a);
 
