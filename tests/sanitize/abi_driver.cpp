@@ -214,11 +214,36 @@ void masked_cases() {
     stub::calls = 0;
     expect("masked valid", attn_fwd_masked(&q, &k, &v, m, ATTN_MASK_ADDITIVE, 2, 1, 0.f, 0, 8, 8, &o, nullptr, nullptr),
            ATTN_OK);
-    expect_true("masked packed", stub::last == stub::LAUNCH_MASKED && stub::args.mask == m && stub::args.mask_b == 1 &&
-                                     stub::args.mask_h == 0 && stub::args.mask_bool == 0);
+    expect_true("masked packed", stub::last == stub::LAUNCH_MASKED_TUNED && stub::args.mask == m &&
+                                     stub::args.mask_b == 1 && stub::args.mask_h == 0 && stub::args.mask_bool == 0);
+    {
+        // rows that are not 16-byte multiples, or other head dims: the general kernel
+        attn_tensor_t q5 = q, k5 = k, v5 = v, o5 = o;
+        q5.S = k5.S = v5.S = o5.S = 500;
+        expect("masked unaligned rows",
+               attn_fwd_masked(&q5, &k5, &v5, m, ATTN_MASK_ADDITIVE, 1, 1, 0.f, 1, 8, 8, &o5, nullptr, nullptr), ATTN_OK);
+        expect_true("masked unaligned rows: general kernel", stub::last == stub::LAUNCH_MASKED);
+        q5.S = k5.S = v5.S = o5.S = 520;
+        expect("masked bool rows of 520 bytes",
+               attn_fwd_masked(&q5, &k5, &v5, m, ATTN_MASK_BOOL, 1, 1, 0.f, 1, 8, 8, &o5, nullptr, nullptr), ATTN_OK);
+        expect_true("masked bool 520: general kernel", stub::last == stub::LAUNCH_MASKED);
+        expect("masked additive rows of 1040 bytes",
+               attn_fwd_masked(&q5, &k5, &v5, m, ATTN_MASK_ADDITIVE, 1, 1, 0.f, 1, 8, 8, &o5, nullptr, nullptr), ATTN_OK);
+        expect_true("masked additive 520: tuned kernel", stub::last == stub::LAUNCH_MASKED_TUNED);
+        attn_tensor_t q9 = T(0, ATTN_BF16, 1, 256, 2, 96), k9 = T(1, ATTN_BF16, 1, 256, 2, 96),
+                      v9 = T(2, ATTN_BF16, 1, 256, 2, 96), o9 = T(3, ATTN_BF16, 1, 256, 2, 96);
+        expect("masked D96", attn_fwd_masked(&q9, &k9, &v9, m, 0, 1, 1, 0.f, 1, 2, 2, &o9, nullptr, nullptr), ATTN_OK);
+        expect_true("masked D96: general kernel", stub::last == stub::LAUNCH_MASKED);
+        attn_tensor_t qb = T(0, ATTN_BF16, 1, 40000, 1, 64), kb = T(1, ATTN_BF16, 1, 40000, 1, 64),
+                      vb = T(2, ATTN_BF16, 1, 40000, 1, 64), ob = T(3, ATTN_BF16, 1, 40000, 1, 64);
+        expect("masked plane of 3.2 GB", attn_fwd_masked(&qb, &kb, &vb, m, 0, 1, 1, 0.f, 1, 1, 1, &ob, nullptr, nullptr),
+               ATTN_OK);
+        expect_true("masked plane beyond 2^31 bytes: general kernel", stub::last == stub::LAUNCH_MASKED);
+    }
     expect("masked bool", attn_fwd_masked(&q, &k, &v, m, ATTN_MASK_BOOL, 1, 8, 0.f, 1, 8, 8, &o, nullptr, nullptr),
            ATTN_OK);
-    expect_true("masked bool packed", stub::args.mask_bool == 1 && stub::args.mask_b == 0 && stub::args.mask_h == 1);
+    expect_true("masked bool packed", stub::args.mask_bool == 1 && stub::args.mask_b == 0 && stub::args.mask_h == 1 &&
+                                          stub::last == stub::LAUNCH_MASKED_TUNED);
     expect("masked bad type", attn_fwd_masked(&q, &k, &v, m, 5, 1, 1, 0.f, 0, 8, 8, &o, nullptr, nullptr),
            ATTN_ERR_MASK);
     expect("masked bad batch dim", attn_fwd_masked(&q, &k, &v, m, 0, 3, 1, 0.f, 0, 8, 8, &o, nullptr, nullptr),
