@@ -40,7 +40,7 @@ namespace attn_detail {
 
 int launch(const LaunchArgs& a) {
     check(a);
-    if (a.D != 64 && a.D != 128) fail("tuned kernel head dim");
+    if (!attn_detail::tuned_head_dim(a.dtype, a.D)) fail("tuned kernel head dim");
     if (a.cu_seqlens && (a.total < a.S || a.total <= 0)) fail("packed rows");
     stub::args = a;
     stub::last = stub::LAUNCH_FWD;

@@ -19,6 +19,7 @@ ARCH = "gfx950"
 
 # kernels whose MFMAs are inline assembly: their device assembly is checked
 ASM_CHECKED = [f"attn_fwd_{t}_d{d}.hip" for t in ("bf16", "f16", "f32") for d in (64, 128)] + \
+              [f"attn_fwd_{t}_d{d}.hip" for t in ("bf16", "f16") for d in (80, 96, 112)] + \
               [f"attn_fwd_mask_{t}_d{d}.hip" for t in ("bf16", "f16") for d in (64, 128)]
 SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", *ASM_CHECKED, "attn_decode_kernels.hip",
            "attn_masked_kernels.hip"]
@@ -90,6 +91,13 @@ def build(verbose=False, extra_flags=()):
         if lk.returncode != 0:
             sys.stderr.write(lk.stdout + lk.stderr)
             raise RuntimeError(f"link failed with exit code {lk.returncode}")
+        # a shared library links with undefined symbols; a kernel whose host
+        # stub was not emitted would only fail when the library is loaded
+        nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+        missing = [l.split()[-1] for l in nm.stdout.splitlines() if "_GLOBAL__N_" in l]
+        if missing:
+            os.remove(tmp)
+            raise RuntimeError("kernel host stubs missing from the library: " + ", ".join(missing[:5]))
         sys.path.insert(0, PKG)
         try:
             import asm_check

@@ -124,7 +124,7 @@ extern "C" int attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const at
     const int rc = prepare(q, k, v, mask_kind, pad_lens, scale, causal, n_q_heads, n_kv_heads, out, lse,
                            stream, a, empty, true);
     if (rc != ATTN_OK || empty) return rc;
-    if (a.D == 64 || a.D == 128) return attn_detail::launch(a);
+    if (attn_detail::tuned_head_dim(a.dtype, a.D)) return attn_detail::launch(a);
     // other head dims: the general kernel (one workgroup per batch, head and
     // 128-row block; batch on the grid's z axis)
     if (a.B > 65535) return ATTN_ERR_UNSUPPORTED;

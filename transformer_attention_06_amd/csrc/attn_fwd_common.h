@@ -79,6 +79,7 @@ __device__ __forceinline__ void mfma_zero(f32x16& c, const float& a, const float
 // keep() marks values as needed at this point (computed no later); touch()
 // marks a value as redefined here (work using it starts no earlier).
 __device__ __forceinline__ void keep(float x) { asm volatile("" : : "v"(x)); }
+__device__ __forceinline__ void keep_acc(const f32x16& x) { asm volatile("" : : "v"(x)); }
 __device__ __forceinline__ void touch(float& x) { asm volatile("" : "+v"(x)); }
 
 template <typename OP, typename T>

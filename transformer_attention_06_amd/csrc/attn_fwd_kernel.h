@@ -98,15 +98,21 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     constexpr int BN = E::BN;
     constexpr int ES = int(sizeof(T));
     constexpr int CH = 16 / ES;            // elements per 16-byte slot
-    constexpr int NS = D / CH;             // slots per tile row
-    constexpr int ROW_B = D * ES;          // bytes per tile row
-    constexpr int TILE_E = BN * D;         // elements per K (or V) tile
+    // LDS tile rows hold DL head dims, D rounded up to a power of two: with
+    // D < DL (80, 96, 112; 16-bit types) the 16-byte slots at or past D are
+    // loaded as zeros and never read by a K operand; the O blocks past D
+    // multiply zero V columns and are not stored
+    constexpr int DL = D <= 64 ? 64 : 128;
+    static_assert(D % 16 == 0 && D <= DL && (D == DL || sizeof(T) == 2), "head dim");
+    constexpr int NS = DL / CH;            // slots per tile row
+    constexpr int ROW_B = DL * ES;         // bytes per tile row
+    constexpr int TILE_E = BN * DL;        // elements per K (or V) tile
     constexpr int NLD = BN * ROW_B / 4096; // 1 KiB direct loads per wave per tile
     static_assert(NLD * 4096 == BN * ROW_B, "tile split into 1 KiB wave loads");
     constexpr int NC = D / (2 * KPL);      // MFMA steps along D (Sᵀ)
     constexpr int NBLK = BN / 32;          // 32-key blocks per tile
     constexpr int NKC = BN / (2 * KPL);    // MFMA steps along keys (Oᵀ)
-    constexpr int NDB = D / 32;            // 32-dim blocks of O
+    constexpr int NDB = (D + 31) / 32;     // 32-dim blocks of O
     constexpr int NF = 16 * NBLK;          // scores per lane per tile
     constexpr int NG = Groups<T, CAUSAL>::value;   // wavefront groups
     constexpr int NBUF = 2;                // LDS buffers per operand and group
@@ -117,7 +123,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     constexpr int PF = 6;                  // operand prefetch distance (MFMAs)
     static_assert(NBUF * TILE_E * ES <= 65536, "buffer offsets fit the LDS immediate");
 
-    // Per group: K tiles [NBUF][BN][D], then V tiles [NBUF][BN][D], slots
+    // Per group: K tiles [NBUF][BN][DL], then V tiles [NBUF][BN][DL], slots
     // swizzled.
     __shared__ __attribute__((aligned(1024))) T lds[NG * 2 * NBUF * TILE_E];
     // Mask tensor tiles: per wavefront 32 rows x BN entries in NML blocks of
@@ -286,6 +292,19 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     const int lr = lane / (ROW_B / 16);
     const int ps = lane % (ROW_B / 16);
     const uint32_t ld_base = uint32_t(lr) * row_bytes + uint32_t((ps ^ swz<NS>(lr)) * 16);
+    // With D < DL the offsets are formed once per load index instead (the
+    // row stride need not be a multiple of the row's 2^k bytes, so the XOR
+    // cannot act on the whole offset), and the padding slots point past the
+    // buffer's end: they read as zero.
+    uint32_t ld_off[D < DL ? NLD : 1];
+    if constexpr (D < DL) {
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int rw = (w4 * NLD + i) * RPL;
+            const int ls = ps ^ swz<NS>(lr) ^ swz<NS>(rw);
+            ld_off[i] = ls < D / CH ? uint32_t(rw + lr) * row_bytes + uint32_t(ls * 16) : 0x80000000u;
+        }
+    }
     const uint32_t lds_k_b = uint32_t(reinterpret_cast<uintptr_t>(lds_k));
     const uint32_t lds_v_b = uint32_t(reinterpret_cast<uintptr_t>(lds_v));
     // Buffer resource of one key tile: the slice from key row t·BN on, empty
@@ -305,10 +324,15 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     const uint32_t lds_v_s = __builtin_amdgcn_readfirstlane(lds_v_b);
     // load li (0..NLD-1) of a tile with resource rs into LDS buffer buf
     auto load_part = [&](const i32x4& rs, uint32_t lds_s, int buf, int li) __attribute__((always_inline)) {
-        const int rw = (w4 * NLD + li) * RPL;
-        uint32_t lb = ld_base;
-        asm volatile("" : "+v"(lb));  // formed here, not hoisted as one register per load
-        const uint32_t voff = (lb ^ uint32_t(swz<NS>(rw) * 16)) + uint32_t(rw) * row_bytes;
+        uint32_t voff;
+        if constexpr (D < DL) {
+            voff = ld_off[li];
+        } else {
+            const int rw = (w4 * NLD + li) * RPL;
+            uint32_t lb = ld_base;
+            asm volatile("" : "+v"(lb));  // formed here, not hoisted as one register per load
+            voff = (lb ^ uint32_t(swz<NS>(rw) * 16)) + uint32_t(rw) * row_bytes;
+        }
         lds_dma16(rs, lds_s + uint32_t(buf * TILE_E * ES) + uint32_t((w4 * NLD + li) * 1024), voff);
     };
     // load i (0..2·NLD-1): K tile tk into K buffer kbuf for i < NLD, else V
@@ -330,7 +354,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
     // element offset of this lane's transposing read for (db, h) at kc = 0;
     // key 16·kc + k has the swizzle of k (16·kc ≡ 0 mod 16), so kc only adds
-    // the constant 16·kc·D
+    // the constant 16·kc·DL
     int v_off[NDB][2];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -338,7 +362,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
         for (int h = 0; h < 2; ++h) {
             const int key = 8 * gl + 4 * h + tr_key;
             const int col = 32 * db + tr_col;
-            v_off[db][h] = key * D + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH;
+            v_off[db][h] = key * DL + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH;
         }
     const float sl2 = p.sl2;
 
@@ -429,6 +453,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
+                    if (32 * db + 16 * h >= D) continue;  // padding dims (D % 16 == 0)
                     T vals[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) vals[e] = to_t<T>(oacc[db][8 * h + e] * inv);
@@ -457,7 +482,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
         const int c = i / NBLK, blk = i % NBLK;
         const int col = c * 2 * KPL + gl * KPL;
         const int off = (((col / CH) ^ xk) * CH) + col % CH;
-        return load_op<op_t>(ks + (prow + 32 * blk) * D + off);
+        return load_op<op_t>(ks + (prow + 32 * blk) * DL + off);
     };
     // P·V product i (0..N2-1) of a V tile: key step kc = i / NDB, dim block db
     auto fetch_v = [&](const T* vs, int i) __attribute__((always_inline)) -> op_t {
@@ -465,11 +490,11 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
         if constexpr (KPL == 1) {
             const int key = kidx(kcol, gl);
             const int col = 32 * db + prow;
-            return vs[key * D + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH];
+            return vs[key * DL + (((col / CH) ^ swz<NS>(key)) * CH) + col % CH];
         } else {
             s16x4 half[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) half[h] = lds_read_tr16(vs + 16 * kcol * D + v_off[db][h]);
+            for (int h = 0; h < 2; ++h) half[h] = lds_read_tr16(vs + 16 * kcol * DL + v_off[db][h]);
             return __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
@@ -677,8 +702,8 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
                     const bool G1) __attribute__((always_inline)) {
         const T* kn = lds_k + (1 - par) * TILE_E;
         const T* vc = lds_v + par * TILE_E;
-        constexpr int NL = 2 * NLD;
-        static_assert(N1 % NL == 0, "loads spread evenly over part A");
+        constexpr int NL = 2 * NLD;  // tile loads of a step, spread over part A
+        static_assert(NL <= N1, "one part-A slot per tile load at most");
         op_t fr[PF + 1];
         auto fetch = [&](int g) __attribute__((always_inline)) {
             fr[g % (PF + 1)] = g < N1 ? fetch_k(kn, g) : fetch_v(vc, g - N1);
@@ -692,7 +717,9 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
         for (int i = 0; i < N1; ++i) {
             if (G1) {
                 if (MK != 0 && i == 0) load_mask(t + 1);
-                if (i % (N1 / NL) == 0) load_one(t + KD, t + VD, par, 1 - par, i / (N1 / NL));
+#pragma unroll
+                for (int k = 0; k < NL; ++k)
+                    if (i == k * N1 / NL) load_one(t + KD, t + VD, par, 1 - par, k);
                 if (i + PF < N1 + N2) fetch(i + PF);
                 if (i < NBLK)
                     mfma_zero(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
@@ -841,8 +868,13 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             // last step (t = t1-1): no next tile
             step(t, (t - t0) & 1, sa, sb, false);
             // the output accumulators were last written by MFMAs issued just
-            // now (wait states as after the prologue)
+            // now (wait states as after the prologue); every accumulator
+            // register stays allocated until then, also the padding dims'
+            // ones that are never stored (D < DL), so that no other value
+            // takes a register an MFMA is still writing
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) keep_acc(oacc[db]);
         }
         if (out) write_rows();
     }
@@ -961,6 +993,12 @@ int launch_mask_k(const attn_detail::LaunchArgs& a) {
 template <typename T, int D>
 int launch_mask_d(const attn_detail::LaunchArgs& a) {
     return a.mask_bool ? launch_mask_k<T, D, 2>(a) : launch_mask_k<T, D, 1>(a);
+}
+
+// head dims without the rotary-embedding entry point (80, 96, 112)
+template <typename T, int D>
+int launch_d_plain(const attn_detail::LaunchArgs& a) {
+    return a.lse != nullptr ? launch_r<T, D, true, false>(a) : launch_r<T, D, false, false>(a);
 }
 
 template <typename T, int D>

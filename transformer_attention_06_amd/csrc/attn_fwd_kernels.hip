@@ -124,11 +124,15 @@ int launch_masked_tuned(const LaunchArgs& a) {
 }
 
 int launch(const LaunchArgs& a) {
-    const bool d64 = a.D == 64;
-    switch (a.dtype) {
-        case ATTN_BF16: return d64 ? launch_fwd_bf16_d64(a) : launch_fwd_bf16_d128(a);
-        case ATTN_F16: return d64 ? launch_fwd_f16_d64(a) : launch_fwd_f16_d128(a);
-        default: return d64 ? launch_fwd_f32_d64(a) : launch_fwd_f32_d128(a);
+    const bool bf = a.dtype == ATTN_BF16;
+    switch (a.D) {
+        case 64:
+            return bf ? launch_fwd_bf16_d64(a) : a.dtype == ATTN_F16 ? launch_fwd_f16_d64(a) : launch_fwd_f32_d64(a);
+        case 80: return bf ? launch_fwd_bf16_d80(a) : launch_fwd_f16_d80(a);
+        case 96: return bf ? launch_fwd_bf16_d96(a) : launch_fwd_f16_d96(a);
+        case 112: return bf ? launch_fwd_bf16_d112(a) : launch_fwd_f16_d112(a);
+        default:
+            return bf ? launch_fwd_bf16_d128(a) : a.dtype == ATTN_F16 ? launch_fwd_f16_d128(a) : launch_fwd_f32_d128(a);
     }
 }
 
