@@ -41,6 +41,13 @@ CASES = [
     (9, 224, "bf16", 1, 65, 2, 2, True, None),
     (10, 256, "bf16", 2, 190, 4, 1, True, [190, 33]),
     (11, 256, "fp16", 1, 1, 2, 2, False, None),
+    # the tuned kernel's padded head dims at several query blocks: causal
+    # pairs of heavy and light blocks, their merge, key padding, GQA
+    (12, 144, "bf16", 2, 600, 4, 2, True, [600, 333]),
+    (13, 160, "fp16", 1, 520, 4, 4, True, None),
+    (14, 96, "bf16", 1, 700, 8, 2, True, None),
+    (15, 112, "bf16", 2, 384, 2, 2, False, [384, 200]),
+    (16, 80, "bf16", 1, 1000, 2, 1, True, [1000]),
 ]
 
 
@@ -73,18 +80,20 @@ def test_general_head_dim_masked(D):
     assert_parity(to_np(out), ro, "bf16", lse=lse.cpu().numpy(), lse_ref=rl, what=f"masked D{D}")
 
 
-def test_general_head_dim_writes_only_its_rows():
-    """D = 80 in a buffer row of 80: the output tensor beyond each head's 80
-    dims belongs to the next head, so a sentinel-filled out must hold only
-    attention values (no write past a row) and match the oracle."""
-    B, S, Hq, Hkv, D = 1, 100, 3, 3, 80
+@pytest.mark.parametrize("D", [80, 144])
+def test_general_head_dim_writes_only_its_rows(D):
+    """A head dim below its tile's padded width, in a buffer row of D: the
+    output tensor beyond each head's D dims belongs to the next head, so a
+    sentinel-filled out must hold only attention values (no write past a
+    row) and match the oracle."""
+    B, S, Hq, Hkv = 1, 100, 3, 3
     dev, host = _inputs(30, B, S, Hq, Hkv, D, "fp16")
     out = torch.full_like(dev[0], 7.0)
-    print("general-D sentinel case", flush=True)
+    print(f"general-D sentinel case D{D}", flush=True)
     A.attn_fwd(*dev, A.ATTN_MASK_NONE, None, None, False, Hq, Hkv, out, None)
     torch.cuda.synchronize()
     ro, _ = oracle.attention(*host)
-    assert_parity(to_np(out), ro, "fp16", what="sentinel D80")
+    assert_parity(to_np(out), ro, "fp16", what=f"sentinel D{D}")
 
 
 def test_general_head_dim_fp32_rejected():

@@ -1,0 +1,10 @@
+// attn_fwd_bf16_d144.hip — the __bf16, D = 144 instances of the fused attention
+// forward kernel (attn_fwd_kernel.h; 32-key tiles, LDS rows of 256 dims, the
+// slots past 144 zero); one translation unit per element type and head dim.
+#include "attn_fwd_kernel.h"
+
+namespace attn_detail {
+
+int launch_fwd_bf16_d144(const LaunchArgs& a) { return launch_d_plain<__bf16, 144>(a); }
+
+}  // namespace attn_detail

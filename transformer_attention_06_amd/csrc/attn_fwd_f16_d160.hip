@@ -1,0 +1,10 @@
+// attn_fwd_f16_d160.hip — the _Float16, D = 160 instances of the fused attention
+// forward kernel (attn_fwd_kernel.h; 32-key tiles, LDS rows of 256 dims, the
+// slots past 160 zero); one translation unit per element type and head dim.
+#include "attn_fwd_kernel.h"
+
+namespace attn_detail {
+
+int launch_fwd_f16_d160(const LaunchArgs& a) { return launch_d_plain<_Float16, 160>(a); }
+
+}  // namespace attn_detail

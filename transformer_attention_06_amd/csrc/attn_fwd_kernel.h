@@ -95,14 +95,16 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     using E = Elem<T>;
     using op_t = typename E::op_t;
     constexpr int KPL = E::KPL;
-    constexpr int BN = E::BN;
+    // 64-key tiles; 32 for the 16-bit head dims above 128, whose wider rows
+    // and output accumulators leave room for half the score registers only
+    constexpr int BN = sizeof(T) == 2 && D > 128 ? 32 : E::BN;
     constexpr int ES = int(sizeof(T));
     constexpr int CH = 16 / ES;            // elements per 16-byte slot
     // LDS tile rows hold DL head dims, D rounded up to a power of two: with
-    // D < DL (80, 96, 112; 16-bit types) the 16-byte slots at or past D are
-    // loaded as zeros and never read by a K operand; the O blocks past D
-    // multiply zero V columns and are not stored
-    constexpr int DL = D <= 64 ? 64 : 128;
+    // D < DL (80, 96, 112, 144, 160; 16-bit types) the 16-byte slots at or
+    // past D are loaded as zeros and never read by a K operand; the O
+    // blocks past D multiply zero V columns and are not stored
+    constexpr int DL = D <= 64 ? 64 : D <= 128 ? 128 : 256;
     static_assert(D % 16 == 0 && D <= DL && (D == DL || sizeof(T) == 2), "head dim");
     constexpr int NS = DL / CH;            // slots per tile row
     constexpr int ROW_B = DL * ES;         // bytes per tile row
@@ -882,8 +884,8 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     for (; n_bar < bars_all; ++n_bar) __syncthreads();
 
     // ---- merge the heavy block's two partial states ------------------------
-    // Group 1 leaves (m, l, O) of the heavy block's first nb tiles in LDS (its
-    // own tile buffers, idle now); group 0 combines them with its own:
+    // Group 1 leaves (m, l, O) of the heavy block's first nb tiles in LDS (the
+    // tile buffers, idle now); group 0 combines them with its own:
     // m = max(m0, m1), O = O0·2^(m0-m) + O1·2^(m1-m), likewise the sums.
     if constexpr (NG == 2) {
         if (nb > 0) {
@@ -894,9 +896,12 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             // over the workgroup, so all eight wavefronts arrive here).
             __syncthreads();
             constexpr int GRP_E = 2 * NBUF * TILE_E;  // elements per group region
-            float* stash_o = reinterpret_cast<float*>(lds + GRP_E);
-            float* stash_s = reinterpret_cast<float*>(lds);  // m, l, l_lse (group 0's region)
-            static_assert(4 * 64 * 16 * NDB * 4 <= GRP_E * ES, "O stash fits a group region");
+            // both groups' tile regions are free now: group 1's O at the
+            // start, then its (m, l, l_lse)
+            constexpr int STASH_O = 4 * NDB * 16 * 64;  // floats
+            float* stash_o = reinterpret_cast<float*>(lds);
+            float* stash_s = stash_o + STASH_O;
+            static_assert((STASH_O + 4 * 3 * 64) * 4 <= NG * GRP_E * ES, "merge stash fits the tile regions");
             if (grp == 1) {
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
