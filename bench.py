@@ -641,7 +641,7 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="decode attention over a KV cache (attn_fwd_decode), Llama-2-70B shapes, HBM roofline")
     ap.add_argument("--general-d", action="store_true",
-                    help="head dims other than 64 and 128 (D = 80, 96, 112, 144, 160, 256) at B=1, H=32, S=2048, "
+                    help="head dims other than 64 and 128 (D = 80, 96, 112, 144, 160, 192, 256) at B=1, H=32, S=2048, "
                          "bf16, causal; D = 128 (the tuned kernel) for reference")
     ap.add_argument("--masked", action="store_true",
                     help="additive mask tensor (attn_fwd_masked) on the Llama-2-7B-shaped prefill")
@@ -680,12 +680,13 @@ def main():
         return
     if args.general_d:
         from transformer_attention_06_amd import workloads as W
-        for D in (80, 96, 112, 128, 144, 160, 256):
+        for D in (80, 96, 112, 128, 144, 160, 192, 256):
             w = W.Workload(f"llama2_7b_prefill_d{D}", 1, B=1, S=2048, Hq=32, Hkv=32, D=D, dtype="bf16", causal=True)
             W.WORKLOADS[w.name] = w
             line = bench_one(w.name, args.steps, args.warmup, False, not args.no_graph, warmup_s)
             line["config"]["kernel"] = ("tuned" if D in (64, 128) else "tuned, LDS rows of 128 dims" if D < 128
-                                        else "tuned, 32-key tiles, LDS rows of 256 dims" if D <= 160 else "general")
+                                        else "tuned, 32-key tiles, LDS rows of 256 dims" if D <= 160
+                                        else "tuned, 32-key tiles, one wavefront per SIMD, AGPR accumulators")
             print(json.dumps(line), flush=True)
         return
     if args.masked:

@@ -80,7 +80,8 @@ void fwd_cases() {
         stub::calls = 0;
         expect("fwd general head dim", f.run(), ATTN_OK);
         expect_true("fwd general kernel", stub::last == stub::LAUNCH_GENERAL && stub::calls == 1);
-        for (int64_t d : {int64_t(80), int64_t(96), int64_t(112), int64_t(144), int64_t(160)}) {
+        for (int64_t d : {int64_t(80), int64_t(96), int64_t(112), int64_t(144), int64_t(160), int64_t(192),
+                          int64_t(256)}) {
             Fwd t(ATTN_BF16, 1, 300, 8, 2, d);
             expect("fwd padded head dim", t.run(), ATTN_OK);
             expect_true("fwd padded head dim: tuned kernel", stub::last == stub::LAUNCH_FWD && stub::args.D == d);

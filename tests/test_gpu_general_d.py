@@ -48,6 +48,9 @@ CASES = [
     (14, 96, "bf16", 1, 700, 8, 2, True, None),
     (15, 112, "bf16", 2, 384, 2, 2, False, [384, 200]),
     (16, 80, "bf16", 1, 1000, 2, 1, True, [1000]),
+    (17, 256, "bf16", 1, 700, 4, 2, True, None),
+    (18, 192, "fp16", 2, 333, 2, 1, False, [333, 100]),
+    (19, 256, "fp16", 1, 520, 2, 2, True, [400]),
 ]
 
 

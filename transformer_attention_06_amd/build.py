@@ -19,7 +19,7 @@ ARCH = "gfx950"
 
 # kernels whose MFMAs are inline assembly: their device assembly is checked
 ASM_CHECKED = [f"attn_fwd_{t}_d{d}.hip" for t in ("bf16", "f16", "f32") for d in (64, 128)] + \
-              [f"attn_fwd_{t}_d{d}.hip" for t in ("bf16", "f16") for d in (80, 96, 112, 144, 160)] + \
+              [f"attn_fwd_{t}_d{d}.hip" for t in ("bf16", "f16") for d in (80, 96, 112, 144, 160, 192, 256)] + \
               [f"attn_fwd_mask_{t}_d{d}.hip" for t in ("bf16", "f16") for d in (64, 128)]
 SOURCES = ["attn_api.cpp", "attn_fwd_kernels.hip", *ASM_CHECKED, "attn_decode_kernels.hip",
            "attn_masked_kernels.hip"]

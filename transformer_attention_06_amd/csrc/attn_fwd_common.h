@@ -75,11 +75,42 @@ __device__ __forceinline__ void mfma_zero(f32x16& c, const f16x8& a, const f16x8
 __device__ __forceinline__ void mfma_zero(f32x16& c, const float& a, const float& b) {
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, f32x16{}, 0, 0, 0);
 }
+// The output products with the accumulator in AGPRs (head dims above 160:
+// one wavefront per SIMD, the accumulators beside a full set of VGPRs).
+__device__ __forceinline__ void mfma_acc_a(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_a(f32x16& c, const f16x8& a, const f16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_a(f32x16& c, const float& a, const float& b) { mfma_acc(c, a, b); }
+// Sᵀ products with the Q operand (B) read from AGPRs, where those kernels
+// keep it for the whole loop.
+__device__ __forceinline__ void mfma_acc_qa(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_acc_qa(f32x16& c, const f16x8& a, const f16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_acc_qa(f32x16& c, const float& a, const float& b) { mfma_acc(c, a, b); }
+__device__ __forceinline__ void mfma_zero_qa(f32x16& c, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_zero_qa(f32x16& c, const f16x8& a, const f16x8& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_zero_qa(f32x16& c, const float& a, const float& b) { mfma_zero(c, a, b); }
+// a value made AGPR-resident here (the compiler keeps it there afterwards)
+template <typename V>
+__device__ __forceinline__ void to_agpr(V& x) {
+    asm volatile("" : "+a"(x));
+}
 // Empty assembly statements that fix where VALU work happens in the stream:
 // keep() marks values as needed at this point (computed no later); touch()
 // marks a value as redefined here (work using it starts no earlier).
 __device__ __forceinline__ void keep(float x) { asm volatile("" : : "v"(x)); }
 __device__ __forceinline__ void keep_acc(const f32x16& x) { asm volatile("" : : "v"(x)); }
+__device__ __forceinline__ void keep_acc_a(const f32x16& x) { asm volatile("" : : "a"(x)); }
 __device__ __forceinline__ void touch(float& x) { asm volatile("" : "+v"(x)); }
 
 template <typename OP, typename T>

@@ -62,9 +62,16 @@ static_assert(BM == 4 * 32, "4 wavefronts x 32 rows");
 // sequence costs the same, so independent 4-wave workgroups (two per CU)
 // need no pairing and no shared barrier; fp32 registers do not fit twice per
 // SIMD.
-template <typename T, bool CAUSAL>
+// Head dims above 160 (16-bit types) run one group with one wavefront per
+// SIMD: their output accumulators (8 blocks at D = 256) live in AGPRs
+// beside a full set of VGPRs.
+template <typename T, int D, bool CAUSAL>
 struct Groups {
-    static constexpr int value = sizeof(T) == 2 && CAUSAL ? 2 : 1;
+    static constexpr int value = sizeof(T) == 2 && CAUSAL && D <= 160 ? 2 : 1;
+};
+template <typename T, int D>
+struct WavesPerSimd {
+    static constexpr int value = sizeof(T) == 2 && D > 160 ? 1 : 2;
 };
 
 // Work of one group: one (batch, query head, 128-row query block); four
@@ -91,7 +98,8 @@ struct Groups {
 // step, waited on by that wavefront alone), and adds it to (or selects)
 // the scores of that tile before their row maxima are taken.
 template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE, int MK = 0>
-__global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn_fwd_kernel(KParams p) {
+__global__ __launch_bounds__(kThreads * (Groups<T, D, CAUSAL>::value), (WavesPerSimd<T, D>::value)) void attn_fwd_kernel(
+    KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
     constexpr int KPL = E::KPL;
@@ -105,6 +113,7 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     // past D are loaded as zeros and never read by a K operand; the O
     // blocks past D multiply zero V columns and are not stored
     constexpr int DL = D <= 64 ? 64 : D <= 128 ? 128 : 256;
+    static_assert(D <= 256, "head dim");
     static_assert(D % 16 == 0 && D <= DL && (D == DL || sizeof(T) == 2), "head dim");
     constexpr int NS = DL / CH;            // slots per tile row
     constexpr int ROW_B = DL * ES;         // bytes per tile row
@@ -116,7 +125,8 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
     constexpr int NKC = BN / (2 * KPL);    // MFMA steps along keys (Oᵀ)
     constexpr int NDB = (D + 31) / 32;     // 32-dim blocks of O
     constexpr int NF = 16 * NBLK;          // scores per lane per tile
-    constexpr int NG = Groups<T, CAUSAL>::value;   // wavefront groups
+    constexpr int NG = Groups<T, D, CAUSAL>::value;  // wavefront groups
+    constexpr bool ACC_A = WavesPerSimd<T, D>::value == 1;  // output accumulators in AGPRs
     constexpr int NBUF = 2;                // LDS buffers per operand and group
     constexpr int KD = NBUF == 4 ? 3 : 2;  // step t loads K tile t+KD
     constexpr int VD = NBUF == 4 ? 3 : 1;  // and V tile t+VD
@@ -437,6 +447,10 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
                 }
             }
         }
+        if constexpr (ACC_A) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) to_agpr(qv[c]);
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
         m_run = -INFINITY;
@@ -723,10 +737,17 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
                 for (int k = 0; k < NL; ++k)
                     if (i == k * N1 / NL) load_one(t + KD, t + VD, par, 1 - par, k);
                 if (i + PF < N1 + N2) fetch(i + PF);
-                if (i < NBLK)
-                    mfma_zero(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
-                else
-                    mfma_acc(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                if constexpr (ACC_A) {
+                    if (i < NBLK)
+                        mfma_zero_qa(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                    else
+                        mfma_acc_qa(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                } else {
+                    if (i < NBLK)
+                        mfma_zero(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                    else
+                        mfma_acc(sn[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                }
             }
             if (i == 0) fin();
             if (i > 0) {
@@ -743,7 +764,10 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
 #pragma unroll
         for (int i = 0; i < N2; ++i) {
             if (N1 + i + PF < N1 + N2) fetch(N1 + i + PF);
-            mfma_acc(oacc[i % NDB], fr[(N1 + i) % (PF + 1)], pb[i / NDB]);
+            if constexpr (ACC_A)
+                mfma_acc_a(oacc[i % NDB], fr[(N1 + i) % (PF + 1)], pb[i / NDB]);
+            else
+                mfma_acc(oacc[i % NDB], fr[(N1 + i) % (PF + 1)], pb[i / NDB]);
             // P operand kc (kc >= NKA) is formed over slots [(kc-1)·NDB, kc·NDB)
             if (i / NDB + 1 >= NKA && i / NDB + 1 < NKC) {
                 const int kc = i / NDB + 1, j = i % NDB;
@@ -823,10 +847,17 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
 #pragma unroll
                 for (int i = 0; i < N1; ++i) {
                     if (i + PF < N1) fr[(i + PF) % (PF + 1)] = fetch_k(k0, i + PF);
-                    if (i < NBLK)
-                        mfma_zero(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
-                    else
-                        mfma_acc(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                    if constexpr (ACC_A) {
+                        if (i < NBLK)
+                            mfma_zero_qa(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                        else
+                            mfma_acc_qa(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                    } else {
+                        if (i < NBLK)
+                            mfma_zero(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                        else
+                            mfma_acc(sa[i % NBLK], fr[i % (PF + 1)], qv[i / NBLK]);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -876,7 +907,12 @@ __global__ __launch_bounds__(kThreads * (Groups<T, CAUSAL>::value), 2) void attn
             // takes a register an MFMA is still writing
             asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) keep_acc(oacc[db]);
+            for (int db = 0; db < NDB; ++db) {
+                if constexpr (ACC_A)
+                    keep_acc_a(oacc[db]);
+                else
+                    keep_acc(oacc[db]);
+            }
         }
         if (out) write_rows();
     }
@@ -960,7 +996,7 @@ int launch_t(const attn_detail::LaunchArgs& a) {
     kp.mask_b = a.mask_b;
     kp.mask_h = a.mask_h;
     kp.inv_scale = 1.0f / a.scale;
-    constexpr int NG = Groups<T, CAUSAL>::value;
+    constexpr int NG = Groups<T, D, CAUSAL>::value;
     const int n_tasks = NG == 2 ? (kp.n_qb + 1) / 2 : kp.n_qb;
     const int64_t n_wg = int64_t(n_tasks) * kp.n_units;
     attn_detail::log_launch("attn_fwd_kernel<%s, D=%d, causal=%d, pad=%d, lse=%d, rope=%d, mask=%d> groups=%d "

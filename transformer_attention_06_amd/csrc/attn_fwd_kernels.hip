@@ -133,6 +133,8 @@ int launch(const LaunchArgs& a) {
         case 112: return bf ? launch_fwd_bf16_d112(a) : launch_fwd_f16_d112(a);
         case 144: return bf ? launch_fwd_bf16_d144(a) : launch_fwd_f16_d144(a);
         case 160: return bf ? launch_fwd_bf16_d160(a) : launch_fwd_f16_d160(a);
+        case 192: return bf ? launch_fwd_bf16_d192(a) : launch_fwd_f16_d192(a);
+        case 256: return bf ? launch_fwd_bf16_d256(a) : launch_fwd_f16_d256(a);
         default:
             return bf ? launch_fwd_bf16_d128(a) : a.dtype == ATTN_F16 ? launch_fwd_f16_d128(a) : launch_fwd_f32_d128(a);
     }

@@ -77,7 +77,11 @@ int launch_fwd_f16_d64(const LaunchArgs& a);
 int launch_fwd_f16_d128(const LaunchArgs& a);
 int launch_fwd_f32_d64(const LaunchArgs& a);
 int launch_fwd_f32_d128(const LaunchArgs& a);
-// head dims 80, 96, 112, 144, 160 (16-bit types; no rotary embedding)
+// head dims 80, 96, 112, 144, 160, 192, 256 (16-bit types; no rotary embedding)
+int launch_fwd_bf16_d192(const LaunchArgs& a);
+int launch_fwd_bf16_d256(const LaunchArgs& a);
+int launch_fwd_f16_d192(const LaunchArgs& a);
+int launch_fwd_f16_d256(const LaunchArgs& a);
 int launch_fwd_bf16_d144(const LaunchArgs& a);
 int launch_fwd_bf16_d160(const LaunchArgs& a);
 int launch_fwd_f16_d144(const LaunchArgs& a);
@@ -91,7 +95,7 @@ int launch_fwd_f16_d112(const LaunchArgs& a);
 // head dims the tuned kernel serves for this element type
 inline bool tuned_head_dim(int32_t dtype, int64_t D) {
     return D == 64 || D == 128 ||
-           (dtype != ATTN_F32 && (D == 80 || D == 96 || D == 112 || D == 144 || D == 160));
+           (dtype != ATTN_F32 && (D == 80 || D == 96 || D == 112 || D == 144 || D == 160 || D == 192 || D == 256));
 }
 
 // The tuned kernel with a mask tensor (a.mask; 16-bit types, D = 64 or 128,
