@@ -269,9 +269,12 @@ int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, const attn_ten
  *               between the two launches, so calls that share a workspace
  *               must not overlap.
  *
- * Two launches on `stream`: one workgroup per (256-key chunk, batch, kv head,
- * 32 query rows; 8 for fp32) writes the chunk's partial (O, max, sums); a
- * merge kernel combines the chunks by their log-sum-exp and writes O and LSE.
+ * Launches on `stream`: one workgroup per (split of the cache, batch, kv
+ * head, 32 query rows; for fp32 256-key splits and 8 rows) writes the split's
+ * partial (O, max, sums) to the workspace, and a merge kernel combines the
+ * splits by their log-sum-exp and writes O and LSE; for bf16/fp16 the splits
+ * are as few as fill the GPU (never more than the workspace was sized for),
+ * and a call left with one split writes O and LSE directly (one launch).
  * bf16/fp16 run both products on MFMA with fp32 accumulation, P rounded to
  * the input type, O normalised by the sum of the rounded probabilities and
  * LSE taken from the exact sum.

@@ -12,26 +12,29 @@
 // from bytes and FLOPs first), so the design goal is to read every cached
 // byte once, coalesced, from as many workgroups as the chip has:
 //
-//   * one workgroup per (key chunk of 256, batch, kv head, group of query
+//   * one workgroup per (split of the cache, batch, kv head, group of query
 //     rows): all query heads sharing the kv head are rows of the same
-//     workgroup, so K and V are read once per chunk;
+//     workgroup, so K and V are read once per split;
 //   * 16-bit types: the query rows of a kv head (8 for a Llama-2-70B-style
-//     8:1 GQA step) against the chunk's keys are a real, if short, dense
+//     8:1 GQA step) against the split's keys are a real, if short, dense
 //     contraction, so both products run on 32x32x16 MFMA exactly as in the
 //     prefill kernel's transposed form (Sᵀ = K·Qᵀ with one query row per
-//     lane, Oᵀ += Vᵀ·Pᵀ): K and Q operands are 16-byte global loads straight
-//     into registers (K rows taken in the permuted order that makes P an MFMA
-//     operand without data movement), V goes through LDS and is read back
-//     with the transposing LDS read.  Each wavefront owns 64 keys, computes
-//     their scores, softmax and P·V in one pass, and the four wavefronts
+//     lane, Oᵀ += Vᵀ·Pᵀ; K rows taken in the permuted order that makes P an
+//     MFMA operand without data movement, V read with the transposing LDS
+//     read).  Splits are as few as fill every CU (so a workgroup spans many
+//     keys) and each of its four wavefronts streams its share in 32-key
+//     chunks through two LDS buffers of its own, loaded straight from global
+//     memory, the next chunk in flight while one is computed; the wavefronts
 //     combine through LDS.  Up to 32 query rows per workgroup;
 //   * fp32 (a parity path): VALU dot products with the head dimension across
-//     lanes, reduced with DPP and lane swaps, 8 query rows per workgroup;
-//   * the chunk's unnormalised (O, max, sum of the rounded probabilities,
-//     exact sum) goes to a caller workspace and a second kernel, one
-//     wavefront per output row, merges the chunks by their log-sum-exp
-//     (O = Σ_s w_s O_s / Σ_s w_s l_s with w_s = 2^(m_s - M)), writing O and
-//     LSE (from the exact sums).
+//     lanes, reduced with DPP and lane swaps, 256-key chunks, 8 query rows
+//     per workgroup;
+//   * with more than one split, each split's unnormalised (O, max, sum of the
+//     rounded probabilities, exact sum) goes to a caller workspace and a
+//     second kernel, one wavefront per output row, merges the splits by
+//     their log-sum-exp (O = Σ_s w_s O_s / Σ_s w_s l_s with w_s = 2^(m_s -
+//     M)), writing O and LSE (from the exact sums); a single split writes O
+//     and LSE itself.
 // The kernel is bound by reading the cache: the MFMAs take a few per cent of
 // the time the cache bytes take at full HBM bandwidth.
 #include <hip/hip_runtime.h>
@@ -48,10 +51,10 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kDecThreads = 256;  // 4 wavefronts
-constexpr int kDecChunk = 256;    // keys per workgroup (64 per wavefront)
+constexpr int kDecThreads = 256;  // 4 wavefronts (fp32 kernel)
+constexpr int kDecChunk = 256;    // keys per workgroup of the fp32 kernel; workspace splits per 256 keys
 constexpr int kDecRows = 8;       // query rows per workgroup (fp32 kernel)
-constexpr int kDecRowsMfma = 32;  // query rows per workgroup (MFMA kernel)
+constexpr int kDecRowsMfma = 32;  // query rows per workgroup (MFMA kernel, 16-bit types)
 constexpr float kDecRescale = 8.0f;
 
 struct DecParams {
@@ -66,6 +69,9 @@ struct DecParams {
     int B, Sq, Sk, Hq, Hkv, G, R, n_split;
     float sl2;  // scale * log2(e)
     int causal;
+    int split_keys;  // streamed kernel: keys per split (a multiple of 128)
+    void* o;         // streamed kernel with one split: the output (B, Sq, Hq, D)
+    float* lse;      // and the LSE (B, Hq, Sq) or null
 };
 
 template <typename T>
@@ -333,202 +339,299 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* ptr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(ptr));
 }
 
+// ---- 16-bit types, streamed ---------------------------------------------------
+// One workgroup per (split of the cache, batch, kv head, 32 query rows), as
+// above, but a split spans many keys and each wavefront streams its share in
+// 32-key chunks through two LDS buffers of its own: K and V rows go straight
+// from global memory to LDS (direct loads, no registers), the loads of chunk
+// c + 1 are in flight while chunk c is computed, and the loads of chunk c + 2
+// are issued as soon as chunk c's operands have been read.  Nothing is shared
+// between the wavefronts until the final combine, so the loop has no
+// barrier.  Per chunk: Sᵀ = K·Qᵀ (one 32-key block, D/16 MFMAs), the online
+// softmax (running max raised only past 2^8, as in the prefill kernel), P
+// packed from the score registers, Oᵀ += Vᵀ·Pᵀ (2·D/32 MFMAs).  With one
+// split the workgroup writes O and LSE itself and no merge is launched.
+constexpr int kStrKeys = 32;   // keys per chunk
+constexpr int kStrWaves = 4;
+
+// XOR swizzle of the 16-byte slots of a K/V row (as in the prefill kernel's
+// tiles): conflict-free row writes, permuted-row operand reads and
+// transposing reads.
+template <int NS>
+__device__ __forceinline__ int str_swz(int row) {
+    if constexpr (NS >= 16)
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    else
+        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte global load per lane into LDS at lds_byte + 16·lane
+// (buffer_load_dwordx4 with LDS destination; M0 holds the LDS address).
+// Assembly: the compiler does not track these writes, so every read of a
+// loaded chunk is ordered by an explicit vmcnt wait of the loading wavefront
+// (each wavefront reads only what it loaded itself).
+__device__ __forceinline__ void str_dma16(const i32x4& rs, uint32_t lds_byte, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_byte), "v"(voff), "s"(rs)
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(n) for the two counts the stream uses
+__device__ __forceinline__ void str_wait(bool next_in_flight, int nld2) {
+    if (next_in_flight) {
+        if (nld2 == 16)
+            asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(kDecThreads, 2) void decode_mfma_kernel(DecParams p) {
+__global__ __launch_bounds__(kStrWaves * 64, 1) void decode_stream_kernel(DecParams p) {
     using op_t = typename MfmaOp<T>::op_t;
-    constexpr int KW = kDecChunk / 4;  // keys per wavefront (64)
-    constexpr int NC = D / 16;         // MFMA steps along D for Sᵀ
-    constexpr int NDB = D / 32;        // 32-dim blocks of Oᵀ
-    constexpr int ROWP = D + 8;        // LDS row pitch of the V tile (elements): rows shift by 16 bytes
-    constexpr int CPR = D / 8;         // 16-byte chunks per cache row
-    constexpr int NVL = KW * CPR / 64; // V chunks per lane
-    static_assert(4 * NDB * 16 * 64 * 4 <= 4 * KW * ROWP * int(sizeof(T)), "combine stash fits the V tiles");
-    __shared__ __attribute__((aligned(16))) T vt[4 * KW * ROWP];
-    __shared__ float s_ml[4][3][64];
+    constexpr int CH = 8;                       // elements per 16-byte slot
+    constexpr int NS = D / CH;                  // slots per row
+    constexpr int ROW_B = D * 2;                // bytes per row
+    constexpr int TILE_E = kStrKeys * D;        // elements per K (or V) chunk
+    constexpr int NLD = kStrKeys * ROW_B / 1024;  // 1 KiB loads per chunk tile
+    constexpr int RPL = 1024 / ROW_B;           // rows per load
+    constexpr int NC = D / 16;                  // Sᵀ MFMAs per chunk
+    constexpr int NDB = D / 32;                 // 32-dim blocks of O
+    static_assert(NLD * 1024 == kStrKeys * ROW_B && 2 * NLD <= 16, "chunk loads");
+    // per wavefront: buffers 0 and 1, each a K tile then a V tile
+    __shared__ __attribute__((aligned(1024))) T lds[kStrWaves * 2 * 2 * TILE_E];
+    __shared__ float s_ml[kStrWaves][3][64];
+    static_assert(kStrWaves * NDB * 16 * 64 * 4 <= int(sizeof(lds)), "combine stash fits the tiles");
 
     const int split = blockIdx.x;
     const int bg = blockIdx.y;  // b * Hkv + g
     const int rg = blockIdx.z;  // group of 32 query rows
     const int b = bg / p.Hkv, g = bg % p.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     const int r = lane & 31, gl = lane >> 5;
     int L = p.lens ? p.lens[b] : p.Sk;
     L = L < 0 ? 0 : (L > p.Sk ? p.Sk : L);
-    const int k0 = split * kDecChunk + wave * KW;  // this wavefront's first key
 
-    // this lane's query row (the same for both halves of the wavefront)
     const int rr = rg * kDecRowsMfma + r;
     const bool live = rr < p.R;
     const int hq = g * p.G + (live ? rr / p.Sq : 0);
     const int tok = live ? rr % p.Sq : 0;
-    int jend = 0;  // keys j < jend are visible to this row (end-aligned causal rule)
+    int jend = 0;  // keys j < jend are visible to this row
     if (live) {
         jend = p.causal ? L - p.Sq + tok + 1 : L;
         jend = jend < 0 ? 0 : (jend > L ? L : jend);
     }
 
-    const int64_t kv_row = int64_t(p.Hkv) * D;  // elements between cache rows
-    const T* kb = static_cast<const T*>(p.k) + (int64_t(b) * p.Sk * p.Hkv + g) * D;
-    const T* vb = static_cast<const T*>(p.v) + (int64_t(b) * p.Sk * p.Hkv + g) * D;
-    T* vw = vt + wave * KW * ROWP;
+    // this wavefront's keys: [w0, w1), in chunks of 32
+    const int per_wave = p.split_keys / kStrWaves;
+    const int w0 = split * p.split_keys + wave * per_wave;
+    int w1 = w0 + per_wave;
+    w1 = w1 < L ? w1 : L;
+    const int n_ch = w1 > w0 ? (w1 - w0 + kStrKeys - 1) / kStrKeys : 0;
 
-    // Loads without branches, so that every load of the wavefront is in
-    // flight at once: cache rows past L are read as row L-1 (their scores
-    // are hidden, so they only meet P = 0), and a wavefront whose 64 keys
-    // all lie past L loads nothing (a wavefront-uniform branch).
-    const bool any = k0 < L;
-    const int klast = L - 1;
-    // V: the wavefront's 64 cache rows into its LDS tile
-    u32x4 vreg[NVL];
-    // K operands: block blk, virtual row r is key k0 + 32·blk + perm_row(r);
-    // the lane holds head dims 16c + 8gl .. +7
-    op_t kop[2][NC];
-    if (any) {
-#pragma unroll
-        for (int i = 0; i < NVL; ++i) {
-            const int ch = lane + 64 * i, key = k0 + ch / CPR, c8 = ch % CPR;
-            vreg[i] = *reinterpret_cast<const u32x4*>(vb + int64_t(key < L ? key : klast) * kv_row + 8 * c8);
-        }
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int key = k0 + 32 * blk + perm_row(r);
-            const T* kr = kb + int64_t(key < L ? key : klast) * kv_row + 8 * gl;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) kop[blk][c] = *reinterpret_cast<const op_t*>(kr + 16 * c);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NVL; ++i) vreg[i] = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) kop[blk][c] = op_t{};
-    }
-    // Q operand: the lane's row, head dims 16c + 8gl .. +7 (rows past the
-    // group read the group's first row: their keys are all hidden and their
-    // results are never written)
+    // Q operand of the lane's row: head dims 16c + 8gl .. +7 (rows past the
+    // group read the group's first row; their results are never written);
+    // loaded before any chunk so that its wait covers nothing else
     op_t qop[NC];
     const T* qr = static_cast<const T*>(p.q) + ((int64_t(b) * p.Sq + tok) * p.Hq + hq) * D + 8 * gl;
 #pragma unroll
     for (int c = 0; c < NC; ++c) qop[c] = *reinterpret_cast<const op_t*>(qr + 16 * c);
-
 #pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-        const int ch = lane + 64 * i;
-        *reinterpret_cast<u32x4*>(vw + (ch / CPR) * ROWP + 8 * (ch % CPR)) = vreg[i];
+    for (int c = 0; c < NC; ++c) asm volatile("" : "+v"(qop[c]));
+
+    // loads: rows k0 + [0, 32) of this (batch, kv head) slice, through a
+    // resource ending after row L - 1 (rows at or past L read as zero)
+    const uint32_t row_stride = uint32_t(p.Hkv) * uint32_t(ROW_B);
+    const T* kbase = static_cast<const T*>(p.k) + (int64_t(b) * p.Sk * p.Hkv + g) * D;
+    const T* vbase = static_cast<const T*>(p.v) + (int64_t(b) * p.Sk * p.Hkv + g) * D;
+    const int lr = lane / (ROW_B / 16), ps = lane % (ROW_B / 16);
+    uint32_t voff[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int row = i * RPL + lr;
+        voff[i] = uint32_t(row) * row_stride + uint32_t((ps ^ str_swz<NS>(row)) * 16);
     }
+    const uint32_t lds_w = __builtin_amdgcn_readfirstlane(
+        uint32_t(reinterpret_cast<uintptr_t>(lds)) + uint32_t(wave * 2 * 2 * TILE_E * 2));
+    auto issue = [&](int c) __attribute__((always_inline)) {
+        const int k0 = w0 + c * kStrKeys;
+        const int valid = L - k0 < kStrKeys ? L - k0 : kStrKeys;  // >= 1: k0 < L
+        const uint32_t rec = uint32_t(valid - 1) * row_stride + uint32_t(ROW_B);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint64_t a = reinterpret_cast<uint64_t>(t == 0 ? kbase : vbase) + uint64_t(k0) * row_stride;
+            const i32x4 rs{__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
+                           __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffff)),
+                           __builtin_amdgcn_readfirstlane(int(rec)), 0x00020000};
+            const uint32_t dst = lds_w + uint32_t((((c & 1) * 2 + t) * TILE_E) * 2);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) str_dma16(rs, dst + uint32_t(i * 1024), voff[i]);
+        }
+    };
 
-    // Sᵀ = K·Qᵀ for the 64 keys
-    f32x16 sacc[2];
+    // per-lane LDS read offsets (elements within a tile)
+    const int prow = perm_row(r);
+    const int xk = str_swz<NS>(prow);
+    const int tr_key = (r & 15) >> 2;
+    const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
+    int v_off[NDB][2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-        sacc[blk] = f32x16{};
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) sacc[blk] = MfmaOp<T>::mma(kop[blk][c], qop[c], sacc[blk]);
-    }
+        for (int h = 0; h < 2; ++h) {
+            const int key = 8 * gl + 4 * h + tr_key;
+            const int col = 32 * db + tr_col;
+            v_off[db][h] = key * D + (((col / CH) ^ str_swz<NS>(key)) * CH) + col % CH;
+        }
+    const T* lds_wave = lds + wave * 2 * 2 * TILE_E;
 
-    // softmax over the wavefront's keys (scores in log2 units)
-    float mx = -INFINITY;
+    f32x16 oacc[NDB];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f, e_run = 0.0f;
+
+    if (n_ch > 0) issue(0);
+    if (n_ch > 1) issue(1);
+    for (int c = 0; c < n_ch; ++c) {
+        str_wait(c + 1 < n_ch, 2 * NLD);  // chunk c landed (chunk c + 1 may still be in flight)
+        const T* kt = lds_wave + (c & 1) * 2 * TILE_E;
+        const T* vt = kt + TILE_E;
+        const int k0 = w0 + c * kStrKeys;
+        // Sᵀ: virtual row r of the block is key k0 + perm_row(r)
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const op_t ka = *reinterpret_cast<const op_t*>(kt + prow * D + (((2 * cc + gl) ^ xk) * CH));
+            sacc = MfmaOp<T>::mma(ka, qop[cc], sacc);
+        }
+        // scores in log2 units, hidden keys -inf; this chunk's row max
+        float mx = -INFINITY;
 #pragma unroll
         for (int f = 0; f < 16; ++f) {
-            const int key = k0 + 32 * blk + acc_pos(f, gl);
-            const float sv = key < jend ? sacc[blk][f] * p.sl2 : -INFINITY;
-            sacc[blk][f] = sv;
+            const int key = k0 + acc_pos(f, gl);
+            const float sv = key < jend ? sacc[f] * p.sl2 : -INFINITY;
+            sacc[f] = sv;
             mx = fmaxf(mx, sv);
         }
-    mx = fmaxf(mx, xor32(mx));
-    const float mu = mx == -INFINITY ? 0.0f : mx;
-    float lsum = 0.0f, lex = 0.0f;
-    op_t pop[2][2];  // P operand of block blk, 16-key step kc: registers 8kc .. 8kc+7
+        mx = fmaxf(mx, xor32(mx));
+        // raise the running max only when some row of the wavefront gains
+        // more than 2^8 (the exponentials then stay below 2^8)
+        const bool resc = __builtin_amdgcn_ballot_w64(mx > m_run + kDecRescale) != 0;
+        if (resc) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+            e_run *= alpha;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            m_run = m_new;
+        }
+        const float mu = m_run == -INFINITY ? 0.0f : m_run;
+        op_t pop[2];  // P operand of 16-key step kc: registers 8kc .. 8kc+7
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(sacc[blk][8 * kc + e] - mu);
+                const float pe = __builtin_amdgcn_exp2f(sacc[8 * kc + e] - mu);
                 const T pr = static_cast<T>(pe);
-                lex += pe;
-                lsum += float(pr);
-                pop[blk][kc][e] = pr;
+                e_run += pe;
+                l_run += float(pr);
+                pop[kc][e] = pr;
             }
-    lsum += xor32(lsum);
-    lex += xor32(lex);
-
-    // the tile was written by this wavefront's own lanes: wait for the writes
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-
-    // Oᵀ += Vᵀ·Pᵀ: Vᵀ rows (head dims) in the permuted order, read transposed
-    const int tr_key = (r & 15) >> 2;
-    const int tr_col = 16 * (r >> 4) + 4 * (((r & 1) << 1) | ((r >> 1) & 1));
-    f32x16 oacc[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+        // Oᵀ += Vᵀ·Pᵀ
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 s16x4 half[2];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int key = 32 * blk + 16 * kc + 8 * gl + 4 * h + tr_key;
-                    half[h] = lds_read_tr16(vw + key * ROWP + 32 * db + tr_col);
-                }
-                const op_t va = __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[db] = MfmaOp<T>::mma(va, pop[blk][kc], oacc[db]);
+                for (int h = 0; h < 2; ++h) half[h] = lds_read_tr16(vt + 16 * kc * D + v_off[db][h]);
+                const op_t va =
+                    __builtin_bit_cast(op_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = MfmaOp<T>::mma(va, pop[kc], oacc[db]);
             }
+        // this chunk's operands are read: its buffers take chunk c + 2
+        if (c + 2 < n_ch) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            issue(c + 2);
+        }
+    }
+    // rows' sums over both halves of the wavefront (keys 8gl .. of each block)
+    l_run += xor32(l_run);
+    e_run += xor32(e_run);
 
-    // combine the four wavefronts: (m, l, l_exact) and Oᵀ through LDS (the V
-    // tiles are free once every wavefront has passed the barrier)
+    // combine the four wavefronts through LDS (every chunk's loads have
+    // landed: the last wait was vmcnt(0))
     __syncthreads();
-    float* stash = reinterpret_cast<float*>(vt);
+    float* stash = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int f = 0; f < 16; ++f) stash[((wave * NDB + db) * 16 + f) * 64 + lane] = oacc[db][f];
-    s_ml[wave][0][lane] = mx;
-    s_ml[wave][1][lane] = lsum;
-    s_ml[wave][2][lane] = lex;
+    s_ml[wave][0][lane] = m_run;
+    s_ml[wave][1][lane] = l_run;
+    s_ml[wave][2][lane] = e_run;
     __syncthreads();
     if (wave < NDB && live) {
         const int db = wave;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][lane]);
-        float wt[4], lt = 0.0f, et = 0.0f;
+        for (int w = 0; w < kStrWaves; ++w) M = fmaxf(M, s_ml[w][0][lane]);
+        float wt[kStrWaves], lt = 0.0f, et = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < kStrWaves; ++w) {
             wt[w] = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(s_ml[w][0][lane] - M);
             lt += wt[w] * s_ml[w][1][lane];
             et += wt[w] * s_ml[w][2][lane];
         }
-        const int64_t pi = ((int64_t(split) * p.B + b) * p.Hq + hq) * p.Sq + tok;
-        float* dst = p.ws_o + pi * D + 32 * db + 8 * gl;
+        if (p.n_split == 1) {
+            // the whole cache in this workgroup: O and LSE directly
+            const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+            T* orow = static_cast<T*>(p.o) + ((int64_t(b) * p.Sq + tok) * p.Hq + hq) * D + 32 * db + 8 * gl;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float o8[8];
+            for (int h = 0; h < 2; ++h) {
+                T o8[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int f = 8 * h + e;
-                float acc = 0.0f;
+                for (int e = 0; e < 8; ++e) {
+                    const int f = 8 * h + e;
+                    float acc = 0.0f;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) acc += wt[w] * stash[((w * NDB + db) * 16 + f) * 64 + lane];
-                o8[e] = acc;
+                    for (int w = 0; w < kStrWaves; ++w) acc += wt[w] * stash[((w * NDB + db) * 16 + f) * 64 + lane];
+                    o8[e] = from_f<T>(acc * inv);
+                }
+                *reinterpret_cast<u32x4*>(orow + 16 * h) = *reinterpret_cast<const u32x4*>(o8);
             }
-            // head dims 32db + 16h + 8gl .. +7
-            reinterpret_cast<u32x4*>(dst + 16 * h)[0] = *reinterpret_cast<const u32x4*>(&o8[0]);
-            reinterpret_cast<u32x4*>(dst + 16 * h)[1] = *reinterpret_cast<const u32x4*>(&o8[4]);
-        }
-        if (db == 0 && gl == 0) {
-            p.ws_m[pi] = M;
-            p.ws_l[pi] = lt;
-            p.ws_e[pi] = et;
+            if (db == 0 && gl == 0 && p.lse)
+                p.lse[(int64_t(b) * p.Hq + hq) * p.Sq + tok] =
+                    et > 0.0f ? (M + __builtin_amdgcn_logf(et)) * 0.69314718055994530942f : -INFINITY;
+        } else {
+            const int64_t pi = ((int64_t(split) * p.B + b) * p.Hq + hq) * p.Sq + tok;
+            float* dst = p.ws_o + pi * D + 32 * db + 8 * gl;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float o8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int f = 8 * h + e;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < kStrWaves; ++w) acc += wt[w] * stash[((w * NDB + db) * 16 + f) * 64 + lane];
+                    o8[e] = acc;
+                }
+                reinterpret_cast<u32x4*>(dst + 16 * h)[0] = *reinterpret_cast<const u32x4*>(&o8[0]);
+                reinterpret_cast<u32x4*>(dst + 16 * h)[1] = *reinterpret_cast<const u32x4*>(&o8[4]);
+            }
+            if (db == 0 && gl == 0) {
+                p.ws_m[pi] = M;
+                p.ws_l[pi] = lt;
+                p.ws_e[pi] = et;
+            }
         }
     }
 }
@@ -618,6 +721,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeParams p) {
         p.lse[row] = dex > 0.0f ? (M + __builtin_amdgcn_logf(dex)) * 0.69314718055994530942f : -INFINITY;
 }
 
+// Splits of the streamed kernel: enough workgroups for every CU (256), no
+// more splits than the workspace was sized for (attn_decode_workspace_bytes:
+// one per 256 cached keys), keys per split a multiple of 4 wavefronts x 32.
+inline void stream_splits(int64_t units, int64_t Sk, int max_split, int& n_split, int& split_keys) {
+    int64_t ns = (256 + units - 1) / units;
+    ns = ns < 1 ? 1 : (ns > max_split ? max_split : ns);
+    int64_t sk = (Sk + ns - 1) / ns;
+    sk = (sk + 127) / 128 * 128;
+    sk = sk < 128 ? 128 : sk;
+    split_keys = int(sk);
+    n_split = int(Sk > 0 ? (Sk + sk - 1) / sk : 1);
+}
+
 template <typename T, int D>
 int launch_decode_t(const attn_detail::DecodeArgs& a) {
     DecParams dp;
@@ -626,11 +742,19 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
     dp.v = a.v;
     dp.lens = a.cache_lens;
     const int64_t rows = a.B * a.Hq * a.Sq;
+    int n_split = a.n_split;
+    dp.split_keys = 0;
+    if constexpr (sizeof(T) == 2) {
+        const int64_t n_rg = (int64_t(a.Hq / a.Hkv) * a.Sq + kDecRowsMfma - 1) / kDecRowsMfma;
+        stream_splits(a.B * a.Hkv * n_rg, a.Sk, a.n_split, n_split, dp.split_keys);
+    }
     float* ws = static_cast<float*>(a.workspace);
     dp.ws_o = ws;
-    dp.ws_m = ws + int64_t(a.n_split) * rows * a.D;
-    dp.ws_l = dp.ws_m + int64_t(a.n_split) * rows;
-    dp.ws_e = dp.ws_l + int64_t(a.n_split) * rows;
+    dp.ws_m = ws + int64_t(n_split) * rows * a.D;
+    dp.ws_l = dp.ws_m + int64_t(n_split) * rows;
+    dp.ws_e = dp.ws_l + int64_t(n_split) * rows;
+    dp.o = a.o;
+    dp.lse = a.lse;
     dp.B = int(a.B);
     dp.Sq = int(a.Sq);
     dp.Sk = int(a.Sk);
@@ -638,16 +762,17 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
     dp.Hkv = int(a.Hkv);
     dp.G = int(a.Hq / a.Hkv);
     dp.R = int(dp.G * a.Sq);
-    dp.n_split = a.n_split;
+    dp.n_split = n_split;
     dp.sl2 = a.scale * 1.44269504088896340736f;
     dp.causal = a.causal;
     if constexpr (sizeof(T) == 2) {
         const int n_rg = (dp.R + kDecRowsMfma - 1) / kDecRowsMfma;
-        attn_detail::log_launch("decode_mfma_kernel<%s, D=%d> grid=(%d, %lld, %d) block=%d Sk=%lld Sq=%lld",
-                                attn_detail::dtype_name(a.dtype), D, a.n_split, (long long)(a.B * a.Hkv), n_rg,
-                                kDecThreads, (long long)a.Sk, (long long)a.Sq);
-        hipLaunchKernelGGL((decode_mfma_kernel<T, D>), dim3(unsigned(a.n_split), unsigned(a.B * a.Hkv), unsigned(n_rg)),
-                           dim3(kDecThreads), 0, static_cast<hipStream_t>(a.stream), dp);
+        attn_detail::log_launch("decode_stream_kernel<%s, D=%d> grid=(%d, %lld, %d) block=%d split_keys=%d Sk=%lld "
+                                "Sq=%lld",
+                                attn_detail::dtype_name(a.dtype), D, n_split, (long long)(a.B * a.Hkv), n_rg,
+                                kStrWaves * 64, dp.split_keys, (long long)a.Sk, (long long)a.Sq);
+        hipLaunchKernelGGL((decode_stream_kernel<T, D>), dim3(unsigned(n_split), unsigned(a.B * a.Hkv), unsigned(n_rg)),
+                           dim3(kStrWaves * 64), 0, static_cast<hipStream_t>(a.stream), dp);
     } else {
         const int n_rg = (dp.R + kDecRows - 1) / kDecRows;
         attn_detail::log_launch("decode_split_kernel<%s, D=%d> grid=(%d, %lld, %d) block=%d Sk=%lld Sq=%lld",
@@ -657,7 +782,8 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
                            dim3(kDecThreads), 0, static_cast<hipStream_t>(a.stream), dp);
     }
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess) {
+    // the streamed kernel with one split writes the output itself
+    if (e == hipSuccess && (sizeof(T) == 4 || n_split > 1)) {
         MergeParams mp;
         mp.ws_o = dp.ws_o;
         mp.ws_m = dp.ws_m;
