@@ -240,8 +240,34 @@ def write_traffic(prof_dir, name=DEFAULT_WORKLOAD, out_dir=None):
                ("WRITE_SIZE", f"write_{name}", run),
                ("FETCH_SIZE", "fetch_copy", "--copy-calibration"),
                ("WRITE_SIZE", "write_copy", "--copy-calibration"))]}
-    with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"traffic_{name}.json"), "w") as f:
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
+    with open(os.path.join(out_dir, f"traffic_{name}.json"), "w") as f:
         json.dump(out, f, indent=1)
+    from transformer_attention_06_amd import workloads as W
+    w = W.WORKLOADS[name]
+    pad = W.make_inputs(w)[3] if w.mask_kind else None
+    alg = min_hbm_bytes(w, pad)
+    md = [f"# Device-memory traffic per launch — {name}", "",
+          f"Workload: {name} (B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} {w.dtype}"
+          f"{' causal' if w.causal else ''}{' key-padding' if w.mask_kind else ''}{' LSE' if w.want_lse else ''}).",
+          f"Kernel source sha256[:16]: `{out['kernel_source_sha']}`.", "",
+          "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each in its own rocprofv3 run, from the "
+          "repository root:", ""]
+    md += [f"- `{c}`" for c in out["commands"]]
+    md += ["", f"Summary written by `python3 bench.py --write-traffic {prof_dir} --workload {name}` "
+           f"(`profiles/traffic_{name}.json`).", "",
+           f"Calibration with a plain 512 MiB device copy (`bench.py --copy-calibration`): FETCH_SIZE x{fscale:.4f}, "
+           f"WRITE_SIZE x{wscale:.4f}.", "",
+           "| quantity | value |", "|---|---|",
+           f"| FETCH_SIZE (KiB per dispatch, mean) | {fk:.1f} |",
+           f"| WRITE_SIZE (KiB per dispatch, mean) | {wk:.1f} |",
+           f"| scaled read bytes | {fk * fscale / 1024:.2f} MiB |",
+           f"| scaled write bytes | {wk * wscale / 1024:.2f} MiB |",
+           f"| traffic per launch | {out['traffic_bytes_per_launch'] / 2**20:.2f} MiB |",
+           f"| algorithmic minimum (Q, K, V read once (visible keys), O written once, LSE) | {alg / 2**20:.2f} MiB |",
+           f"| ratio | {out['traffic_bytes_per_launch'] / alg:.3f} |"]
+    with open(os.path.join(out_dir, f"attn_fwd_{name}_traffic.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
     print(json.dumps(out), flush=True)
 
 
