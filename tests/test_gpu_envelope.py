@@ -101,3 +101,10 @@ def test_envelope_long_context_sampled_groups():
     w, host, pad, o, l = _load("long_context")
     rows = np.concatenate([np.arange(s, s + 32) for s in (0, 4096, 8160, 16352)])
     _compare(w, host, pad, o, l, [(0, 0), (0, 31)], rows=rows)
+
+
+def test_envelope_tiny_fp32():
+    """The fp32 path (32-key tiles, P kept in fp32) on the tiny oracle-check
+    workload, both heads, every row."""
+    w, host, pad, o, l = _load("tiny_fp32")
+    _compare(w, host, pad, o, l, [(0, 0), (0, 1)])
