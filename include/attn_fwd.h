@@ -265,16 +265,24 @@ int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, const attn_ten
  *               (lse is (B, Hq, Sq)).
  *   workspace   caller-owned device buffer, 16-byte aligned, of at least
  *               attn_decode_workspace_bytes(B, Sq, Hq, D, Sk) bytes (else
- *               ATTN_ERR_WORKSPACE); it holds per-chunk partial results
- *               between the two launches, so calls that share a workspace
- *               must not overlap.
+ *               ATTN_ERR_WORKSPACE).  Its first 1024 bytes are arrival
+ *               counters: they must be zero before the first call that uses
+ *               the buffer (allocate it zero-filled, or clear it once), and
+ *               every call leaves them zero again, so a buffer can serve any
+ *               number of calls of any sizes it is large enough for.  The
+ *               rest holds per-split partial results during a call and
+ *               needs no initialisation.  Calls that share a workspace must
+ *               not overlap (same stream, or otherwise ordered).
  *
  * Launches on `stream`: one workgroup per (split of the cache, batch, kv
  * head, 32 query rows; for fp32 256-key splits and 8 rows) writes the split's
- * partial (O, max, sums) to the workspace, and a merge kernel combines the
- * splits by their log-sum-exp and writes O and LSE; for bf16/fp16 the splits
- * are as few as fill the GPU (never more than the workspace was sized for),
- * and a call left with one split writes O and LSE directly (one launch).
+ * partial (O, max, sums) to the workspace, and the splits are combined by
+ * their log-sum-exp into O and LSE.  For bf16/fp16 the splits are as few as
+ * fill the GPU (never more than the workspace was sized for); a call left
+ * with one split writes O and LSE directly, and with up to 8 splits the last
+ * split of each (batch, kv head, 32 query rows) to finish (counted in the
+ * workspace's counters, which it returns to zero) merges them: one launch.
+ * With more splits, and for fp32, a second kernel merges.
  * bf16/fp16 run both products on MFMA with fp32 accumulation, P rounded to
  * the input type, O normalised by the sum of the rounded probabilities and
  * LSE taken from the exact sum.
@@ -296,18 +304,22 @@ int attn_fwd_decode(const attn_tensor_t* q, const attn_tensor_t* k_cache, const 
  * 33554432 return ATTN_ERR_SCRATCH (before any HIP call).  The array's device
  * address is looked up (no allocation) on the first call on each device.
  *
- * Every call on one GPU shares that GPU's array and leaves its contents
- * behind; each call writes every entry it reads, so nothing needs clearing.
- * Calls that may overlap on one GPU (concurrent streams, threads) race on the
- * array: serialise them.  Nothing is allocated or freed by this call.
+ * Every call on one GPU shares that GPU's array.  Its arrival counters (the
+ * first 1024 bytes, as in a caller workspace) are zero when the library is
+ * loaded (a zero-initialised device array) and every call leaves them zero;
+ * the partial results each call reads are ones it wrote itself, so nothing
+ * needs clearing.  Calls that may overlap on one GPU (concurrent streams,
+ * threads) race on the array: serialise them.  Nothing is allocated or freed
+ * by this call.
  */
 int attn_fwd_decode_noalloc(const attn_tensor_t* q, const attn_tensor_t* k_cache, const attn_tensor_t* v_cache,
                             const int32_t* cache_lens, float scale, int causal, int n_q_heads, int n_kv_heads,
                             const attn_tensor_t* out, float* lse, void* stream);
 
-/* Bytes of workspace attn_fwd_decode needs for these sizes: one 256-key chunk
- * (at least one, also for an empty cache) × B·Hq·Sq rows × (D + 3) floats;
- * -1 if a size is negative or the count does not fit in int64. */
+/* Bytes of workspace attn_fwd_decode needs for these sizes: 1024 bytes of
+ * arrival counters, then one 256-key chunk (at least one, also for an empty
+ * cache) × B·Hq·Sq rows × (D + 3) floats; -1 if a size is negative or the
+ * count does not fit in int64. */
 int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_heads, int64_t D, int64_t Sk);
 
 /* Static, human-readable text for a return code (never NULL). */

@@ -330,10 +330,12 @@ void rope_cases() {
 void decode_cases() {
     const int64_t big = std::numeric_limits<int64_t>::max();
     expect("workspace negative", int(attn_decode_workspace_bytes(-1, 1, 8, 128, 10)), -1);
-    expect_true("workspace value", attn_decode_workspace_bytes(2, 3, 8, 128, 1000) == 4 * 2 * 8 * 3 * 131 * 4);
-    expect_true("workspace empty cache", attn_decode_workspace_bytes(1, 1, 1, 64, 0) == 67 * 4);
+    expect_true("workspace value", attn_decode_workspace_bytes(2, 3, 8, 128, 1000) == 1024 + 4 * 2 * 8 * 3 * 131 * 4);
+    expect_true("workspace empty cache", attn_decode_workspace_bytes(1, 1, 1, 64, 0) == 1024 + 67 * 4);
     expect_true("workspace overflow", attn_decode_workspace_bytes(big, big, 65535, 128, big) == -1);
     expect_true("workspace overflow D", attn_decode_workspace_bytes(1, 1, 1, big, 10) == -1);
+    // partials fit int64 (4 * (big / 4) = big - 3), the counter header does not
+    expect_true("workspace overflow by the counters", attn_decode_workspace_bytes(1, 1, 1, big / 4 - 3, 0) == -1);
     expect_true("workspace overflow near the edge",
                 attn_decode_workspace_bytes(int64_t(1) << 30, int64_t(1) << 19, 65535, 256, (int64_t(1) << 29) - 1) ==
                     -1);

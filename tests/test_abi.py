@@ -226,11 +226,13 @@ def call_dec(lib, q, k, v, out, lens=None, causal=1, ws=FAKE + 0x100000, ws_byte
 
 
 def test_decode_workspace_bytes(lib):
-    # 256-key chunks x rows x (D + 3) floats
-    assert A.decode_workspace_bytes(2, 1, 64, 128, 4096) == 16 * 2 * 64 * 1 * 131 * 4
-    assert A.decode_workspace_bytes(1, 3, 8, 64, 1) == 1 * 1 * 8 * 3 * 67 * 4
-    assert A.decode_workspace_bytes(1, 3, 8, 64, 257) == 2 * 1 * 8 * 3 * 67 * 4
-    assert A.decode_workspace_bytes(1, 3, 8, 64, 0) == 1 * 1 * 8 * 3 * 67 * 4  # empty cache: one chunk
+    # 1 KiB of arrival counters, then 256-key chunks x rows x (D + 3) floats
+    c = A.DECODE_COUNTER_BYTES
+    assert c == 1024
+    assert A.decode_workspace_bytes(2, 1, 64, 128, 4096) == c + 16 * 2 * 64 * 1 * 131 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 1) == c + 1 * 1 * 8 * 3 * 67 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 257) == c + 2 * 1 * 8 * 3 * 67 * 4
+    assert A.decode_workspace_bytes(1, 3, 8, 64, 0) == c + 1 * 1 * 8 * 3 * 67 * 4  # empty cache: one chunk
     assert lib.attn_decode_workspace_bytes(-1, 1, 1, 64, 1) == -1
 
 
@@ -277,7 +279,7 @@ def test_decode_noalloc_checks(lib):
 
 def test_decode_noalloc_rejects_sizes_beyond_its_workspace(lib):
     limit = 32 << 20
-    # B=8, Hq=64, D=128, Sk=4096: 16 chunks x 512 rows x 131 floats = 4.3 MB, within the limit
+    # B=8, Hq=64, D=128, Sk=4096: 1 KiB + 16 chunks x 512 rows x 131 floats = 4.3 MB, within the limit
     assert A.decode_workspace_bytes(8, 1, 64, 128, 4096) <= limit
     # 16 times the cache: 68.7 MB, beyond it
     big = dict(B=8, H=8, D=128)

@@ -81,3 +81,55 @@ def test_decode_scale_and_prefill_tail():
     torch.cuda.synchronize()
     ro, _ = oracle.attention(qn, kn, vn, causal=True, scale=0.07)
     assert_parity(to_np(od), ro, "bf16", what="decode Sq == Sk")
+
+
+def test_decode_workspace_reused_across_shapes_keeps_counters_zero():
+    """One zero-filled workspace serves calls of different shapes (4, 16, 79
+    and one split per row group; its partial area holding the last call's
+    values, or NaN bytes): every call matches the oracle and leaves the
+    arrival counters at the head of the workspace zero."""
+    shapes = [  # seed, B, Sq, Sk, Hq, Hkv, D, dtype
+        (20, 8, 1, 4096, 64, 8, 128, "bf16"),    # 4 splits per row group
+        (21, 2, 1, 4096, 64, 8, 128, "bf16"),    # 16 splits
+        (22, 1, 1, 20000, 8, 2, 128, "fp16"),    # 79 splits: ten batches of the merge's loads
+        (23, 16, 1, 4096, 32, 32, 64, "bf16"),   # 512 row groups: one split, no counter
+        (24, 8, 1, 4096, 64, 8, 128, "bf16"),    # the first shape again
+    ]
+    need = max(A.decode_workspace_bytes(B, Sq, Hq, D, Sk) for _, B, Sq, Sk, Hq, Hkv, D, _ in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws[A.DECODE_COUNTER_BYTES:] = 0xFF  # partial area: NaN floats before the first call
+    for seed, B, Sq, Sk, Hq, Hkv, D, dtype in shapes:
+        rng = np.random.default_rng(seed)
+        qd, qn = prep(rng.standard_normal((B, Sq, Hq, D)).astype(np.float32), dtype)
+        kd, kn = prep(rng.standard_normal((B, Sk, Hkv, D)).astype(np.float32), dtype)
+        vd, vn = prep(rng.standard_normal((B, Sk, Hkv, D)).astype(np.float32), dtype)
+        out = torch.empty_like(qd)
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+        print(f"decode workspace reuse seed={seed} B{B} Sk{Sk} H{Hq}/{Hkv} D{D} {dtype}", flush=True)
+        A.attn_fwd_decode(qd, kd, vd, None, None, True, Hq, Hkv, out, lse, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:A.DECODE_COUNTER_BYTES].count_nonzero()) == 0, f"counters left nonzero after seed {seed}"
+        ro, rl = oracle.attention_decode(qn, kn, vn, causal=True)
+        assert_parity(to_np(out), ro, dtype, lse=to_np(lse), lse_ref=rl, what=f"decode reuse seed {seed}")
+
+
+def test_decode_repeated_calls_same_result():
+    """Back-to-back calls on one workspace (no synchronisation between them):
+    each call's last split per row group merges, so every call's output is
+    the same, bit for bit."""
+    rng = np.random.default_rng(25)
+    B, Sk, Hq, Hkv, D = 2, 4096, 64, 8, 128
+    qd, _ = prep(rng.standard_normal((B, 1, Hq, D)).astype(np.float32), "bf16")
+    kd, _ = prep(rng.standard_normal((B, Sk, Hkv, D)).astype(np.float32), "bf16")
+    vd, _ = prep(rng.standard_normal((B, Sk, Hkv, D)).astype(np.float32), "bf16")
+    ws = torch.zeros(A.decode_workspace_bytes(B, 1, Hq, D, Sk), dtype=torch.uint8, device="cuda")
+    outs = []
+    print("decode repeated calls B2 Sk4096", flush=True)
+    for _ in range(6):
+        out = torch.empty_like(qd)
+        A.attn_fwd_decode(qd, kd, vd, None, None, True, Hq, Hkv, out, None, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    assert int(ws[:A.DECODE_COUNTER_BYTES].count_nonzero()) == 0

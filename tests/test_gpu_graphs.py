@@ -46,7 +46,7 @@ def test_graph_decode():
     ref_o, ref_l = A.decode_attention(q, k, v, cache_lens=lens, return_lse=True)
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
-    ws = torch.empty(A.decode_workspace_bytes(B, Sq, Hq, D, Sk), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(A.decode_workspace_bytes(B, Sq, Hq, D, Sk), dtype=torch.uint8, device="cuda")
     print("graph case decode", flush=True)
     _replays(lambda: A.attn_fwd_decode(q, k, v, lens, None, True, Hq, Hkv, out, lse, ws), [out, lse],
              [ref_o, ref_l], lambda: A.decode_attention(q, k, v, causal=False))

@@ -34,7 +34,7 @@ def _run_pair(case):
     q, k, v, cl = _inputs(seed, B, Sq, Sk, Hq, Hkv, D, dtype, lens)
     ref_o = torch.full_like(q, float("nan"))
     ref_l = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(A.decode_workspace_bytes(B, Sq, Hq, D, Sk), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(A.decode_workspace_bytes(B, Sq, Hq, D, Sk), dtype=torch.uint8, device="cuda")
     A.attn_fwd_decode(q, k, v, cl, None, causal, Hq, Hkv, ref_o, ref_l, ws)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device="cuda")

@@ -345,8 +345,15 @@ def rope_attention(q, k, v, *, causal=False, pad_lens=None, scale=None, position
     return (out, k_rot, lse) if return_lse else (out, k_rot)
 
 
+# Leading bytes of every decode workspace that hold the arrival counters of
+# the in-kernel split merge (zero between calls).
+DECODE_COUNTER_BYTES = 1024
+
+
 def decode_workspace_bytes(B, Sq, n_q_heads, D, Sk):
-    """Bytes of workspace attn_fwd_decode needs."""
+    """Bytes of workspace attn_fwd_decode needs (its first
+    DECODE_COUNTER_BYTES must be zero before the first call; allocate it
+    with torch.zeros and reuse it)."""
     return int(load_library().attn_decode_workspace_bytes(int(B), int(Sq), int(n_q_heads), int(D), int(Sk)))
 
 
@@ -354,7 +361,8 @@ def attn_fwd_decode(q, k_cache, v_cache, cache_lens, scale, causal, n_q_heads, n
                     workspace, stream=None):
     """``attn_fwd_decode`` with torch tensors: q/out (B, Sq, Hq, D), caches
     (B, Sk, Hkv, D), cache_lens int32 [B] or None, workspace a uint8 device
-    tensor of at least decode_workspace_bytes(...) bytes."""
+    tensor of at least decode_workspace_bytes(...) bytes whose first
+    DECODE_COUNTER_BYTES are zero (every call leaves them zero)."""
     import torch
     lib = load_library()
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("workspace", workspace)):
@@ -425,7 +433,7 @@ def decode_attention(q, k_cache, v_cache, *, cache_lens=None, causal=True, scale
     B, Sq, Hq, D = q.shape
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
-    ws = torch.empty(max(16, decode_workspace_bytes(B, Sq, Hq, D, k_cache.shape[1])), dtype=torch.uint8,
+    ws = torch.zeros(max(16, decode_workspace_bytes(B, Sq, Hq, D, k_cache.shape[1])), dtype=torch.uint8,
                      device=q.device)
     attn_fwd_decode(q, k_cache, v_cache, cache_lens, scale, causal, Hq, k_cache.shape[2], out, lse, ws)
     return (out, lse) if return_lse else out

@@ -244,12 +244,14 @@ extern "C" int attn_fwd_rope(const attn_tensor_t* q, const attn_tensor_t* k, con
 // transformer和ATB…" passes the cache into FlashAttention every step).
 extern "C" int64_t attn_decode_workspace_bytes(int64_t B, int64_t Sq, int n_q_heads, int64_t D, int64_t Sk) {
     if (B < 0 || Sq < 0 || n_q_heads < 0 || D < 0 || Sk < 0) return -1;
-    // n_split · B · Hq · Sq · 4 · (D + 3), or -1 where it does not fit int64
+    // the counters, then n_split · B · Hq · Sq · 4 · (D + 3), or -1 where it
+    // does not fit int64
     int64_t r = attn_detail::decode_splits(Sk);
     for (int64_t x : {B, int64_t(n_q_heads), Sq, int64_t(sizeof(float))})
         if (__builtin_mul_overflow(r, x, &r)) return -1;
     int64_t d3 = 0;
     if (__builtin_add_overflow(D, int64_t(3), &d3) || __builtin_mul_overflow(r, d3, &r)) return -1;
+    if (__builtin_add_overflow(r, attn_detail::kDecodeCounterBytes, &r)) return -1;
     return r;
 }
 

@@ -30,11 +30,13 @@
 //     lanes, reduced with DPP and lane swaps, 256-key chunks, 8 query rows
 //     per workgroup;
 //   * with more than one split, each split's unnormalised (O, max, sum of the
-//     rounded probabilities, exact sum) goes to a caller workspace and a
-//     second kernel, one wavefront per output row, merges the splits by
-//     their log-sum-exp (O = Σ_s w_s O_s / Σ_s w_s l_s with w_s = 2^(m_s -
-//     M)), writing O and LSE (from the exact sums); a single split writes O
-//     and LSE itself.
+//     rounded probabilities, exact sum) goes to a caller workspace and the
+//     splits are merged by their log-sum-exp (O = Σ_s w_s O_s / Σ_s w_s l_s
+//     with w_s = 2^(m_s - M)), writing O and LSE (from the exact sums): for
+//     16-bit types with up to 8 splits by the workgroup of each row group
+//     that finishes last (an arrival counter in the workspace, returned to
+//     zero by that workgroup), otherwise by a second kernel; a single split
+//     writes O and LSE itself.
 // The kernel is bound by reading the cache: the MFMAs take a few per cent of
 // the time the cache bytes take at full HBM bandwidth.
 #include <hip/hip_runtime.h>
@@ -70,8 +72,10 @@ struct DecParams {
     float sl2;  // scale * log2(e)
     int causal;
     int split_keys;  // streamed kernel: keys per split (a multiple of 128)
-    void* o;         // streamed kernel with one split: the output (B, Sq, Hq, D)
+    void* o;         // streamed kernel: the output (B, Sq, Hq, D)
     float* lse;      // and the LSE (B, Hq, Sq) or null
+    int* ctr;        // streamed kernel with more than one split: arrival counters,
+                     // one per (batch, kv head, row group), zero on entry and exit
 };
 
 template <typename T>
@@ -350,7 +354,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* ptr) {
 // barrier.  Per chunk: Sᵀ = K·Qᵀ (one 32-key block, D/16 MFMAs), the online
 // softmax (running max raised only past 2^8, as in the prefill kernel), P
 // packed from the score registers, Oᵀ += Vᵀ·Pᵀ (2·D/32 MFMAs).  With one
-// split the workgroup writes O and LSE itself and no merge is launched.
+// split the workgroup writes O and LSE itself; with up to kFoldSplits, the
+// last split of a row group to finish merges them (merge_group): one launch
+// either way.  More splits leave their partials to the merge kernel.
 constexpr int kStrKeys = 32;   // keys per chunk
 constexpr int kStrWaves = 4;
 
@@ -388,6 +394,96 @@ __device__ __forceinline__ void str_wait(bool next_in_flight, int nld2) {
             asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+}
+
+// Device-scope (relaxed) atomic store and load of one float: coherent across
+// the XCDs' L2 caches without cache maintenance.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kCoherent = 16;  // buffer cache policy: device-scope coherent (sc1)
+// Launches of up to this many splits merge inside the split kernel (one
+// round of loads covers them all); more splits are merged by a second
+// kernel, which measured faster there (16 splits: 11.3 against 12.2 µs per
+// Llama-2-70B-shaped call at B = 2, while 4 splits at B = 8 took 26.2 µs
+// folded against 28.5 µs with the second kernel).
+constexpr int kFoldSplits = 8;
+
+// Buffer resource over a partial-output array of n floats (under 2^31 bytes:
+// a launch with more than one split has fewer than 8192 rows and at most 256
+// splits).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const float* base, int64_t n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), short(0), int(n * 4), 0x00020000);
+}
+
+// Merge of the splits of one (batch, kv head, group of 32 query rows) by the
+// workgroup that arrived last: D/4 threads per row, four head dims each,
+// NB splits' partials loaded at a time (device-coherent loads of the
+// group's consecutive partial rows; every load of a batch is in flight at
+// once, so a merge of up to NB splits waits for memory once).  O = Σ_s w_s
+// O_s / Σ_s w_s l_s and LSE from Σ_s w_s e_s, with w_s = 2^(m_s - M) and M
+// the largest m_s (raised batch by batch, rescaling what has been summed).
+template <typename T, int D, int NB>
+__device__ __forceinline__ void merge_group(const DecParams& p, __amdgpu_buffer_rsrc_t o_rs, int b, int g, int rg,
+                                            int n_live, int64_t rows, int64_t grow0) {
+    constexpr int TPR = D / 4;                 // threads per row
+    constexpr int RPI = kStrWaves * 64 / TPR;  // rows per pass
+    const int c4 = threadIdx.x % TPR;
+    const int ns = p.n_split;
+    for (int r = threadIdx.x / TPR; r < n_live; r += RPI) {
+        const int64_t row = grow0 + r;
+        float M = -INFINITY, den = 0.0f, dex = 0.0f;
+        f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s0 = 0; s0 < ns; s0 += NB) {
+            float ms[NB], ls[NB], es[NB];
+            f32x4 o[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const int s = s0 + u < ns ? s0 + u : s0;  // past the last split: re-read a valid one, weight 0
+                const int64_t pi = int64_t(s) * rows + row;
+                ms[u] = coherent_load(p.ws_m + pi);
+                ls[u] = coherent_load(p.ws_l + pi);
+                es[u] = coherent_load(p.ws_e + pi);
+                o[u] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(o_rs, int(uint32_t(pi * D * 4) + uint32_t(c4) * 16u),
+                                                                 0, kCoherent));
+            }
+            float bm = M;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                if (s0 + u >= ns) ms[u] = -INFINITY;
+                bm = fmaxf(bm, ms[u]);
+            }
+            if (bm == -INFINITY) continue;  // no visible key in any split so far
+            const float a = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - bm);
+            den *= a;
+            dex *= a;
+            acc *= a;
+            M = bm;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const float w = ms[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms[u] - M);
+                den += w * ls[u];
+                dex += w * es[u];
+                acc += w * o[u];
+            }
+        }
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        const int rr = rg * kDecRowsMfma + r;
+        const int hq = g * p.G + rr / p.Sq, tok = rr % p.Sq;
+        T o4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = from_f<T>(acc[i] * inv);
+        T* orow = static_cast<T*>(p.o) + ((int64_t(b) * p.Sq + tok) * p.Hq + hq) * D + c4 * 4;
+        *reinterpret_cast<uint64_t*>(orow) = __builtin_bit_cast(uint64_t, o4);
+        if (c4 == 0 && p.lse)
+            p.lse[row] = dex > 0.0f ? (M + __builtin_amdgcn_logf(dex)) * 0.69314718055994530942f : -INFINITY;
     }
 }
 
@@ -570,6 +666,10 @@ __global__ __launch_bounds__(kStrWaves * 64, 1) void decode_stream_kernel(DecPar
     // landed: the last wait was vmcnt(0))
     __syncthreads();
     float* stash = reinterpret_cast<float*>(lds);
+    constexpr int DP = D + 4;  // padded row of the staged partial rows
+    float* c_rows = stash + kStrWaves * NDB * 16 * 64;
+    static_assert((kStrWaves * NDB * 16 * 64 + kDecRowsMfma * DP) * 4 <= int(sizeof(lds)), "staged rows fit");
+    __shared__ float s_part[3][kDecRowsMfma];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -610,7 +710,8 @@ __global__ __launch_bounds__(kStrWaves * 64, 1) void decode_stream_kernel(DecPar
             if (db == 0 && gl == 0 && p.lse)
                 p.lse[(int64_t(b) * p.Hq + hq) * p.Sq + tok] =
                     et > 0.0f ? (M + __builtin_amdgcn_logf(et)) * 0.69314718055994530942f : -INFINITY;
-        } else {
+        } else if (!p.ctr) {
+            // partials for the merge kernel, straight from the registers
             const int64_t pi = ((int64_t(split) * p.B + b) * p.Hq + hq) * p.Sq + tok;
             float* dst = p.ws_o + pi * D + 32 * db + 8 * gl;
 #pragma unroll
@@ -632,13 +733,77 @@ __global__ __launch_bounds__(kStrWaves * 64, 1) void decode_stream_kernel(DecPar
                 p.ws_l[pi] = lt;
                 p.ws_e[pi] = et;
             }
+        } else {
+            // this split's combined rows, row-major, for the coalesced
+            // device-coherent stores below
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int f = 8 * h + e;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < kStrWaves; ++w) acc += wt[w] * stash[((w * NDB + db) * 16 + f) * 64 + lane];
+                    c_rows[r * DP + 32 * db + 8 * gl + 16 * h + e] = acc;
+                }
+            if (db == 0 && gl == 0) {
+                s_part[0][r] = M;
+                s_part[1][r] = lt;
+                s_part[2][r] = et;
+            }
         }
     }
+    if (p.n_split == 1 || !p.ctr) return;
+
+    // More than one split, with arrival counters: this split's partial (O,
+    // max, sums) of the group's live rows goes to the workspace, and the last
+    // split of this (batch, kv head, row group) to arrive merges all of them
+    // and returns the counter to zero for the next call on this workspace.
+    // The group's rows are consecutive rows of the partial arrays, so the
+    // stores and the merge's loads are whole 16-byte vectors, coalesced.
+    // They are device-coherent accesses (sc1), served where all of the chip's
+    // L2 caches agree, so no cache writeback or invalidation is needed (a
+    // device-scope fence writes back and invalidates this XCD's whole L2);
+    // the arrival is counted after every thread's stores have completed, and
+    // the merge's loads are issued after the count.
+    const int n_live = p.R - rg * kDecRowsMfma < kDecRowsMfma ? p.R - rg * kDecRowsMfma : kDecRowsMfma;
+    const int64_t rows = int64_t(p.B) * p.Hq * p.Sq;
+    const int64_t grow0 = (int64_t(b) * p.Hq + int64_t(g) * p.G) * p.Sq + rg * kDecRowsMfma;  // group's first row
+    const __amdgpu_buffer_rsrc_t o_rs = partial_rsrc(p.ws_o, int64_t(p.n_split) * rows * D);
+    __syncthreads();
+    {
+        const uint32_t base = uint32_t((int64_t(split) * rows + grow0) * D * 4);
+        for (int i = threadIdx.x; i * 4 < n_live * D; i += kStrWaves * 64) {
+            const int rw = i * 4 / D, col = i * 4 % D;
+            const i32x4 v = __builtin_bit_cast(i32x4, *reinterpret_cast<const f32x4*>(c_rows + rw * DP + col));
+            __builtin_amdgcn_raw_buffer_store_b128(v, o_rs, int(base + uint32_t(i) * 16u), 0, kCoherent);
+        }
+        if (int(threadIdx.x) < n_live) {
+            const int64_t pi = int64_t(split) * rows + grow0 + threadIdx.x;
+            coherent_store(p.ws_m + pi, s_part[0][threadIdx.x]);
+            coherent_store(p.ws_l + pi, s_part[1][threadIdx.x]);
+            coherent_store(p.ws_e + pi, s_part[2][threadIdx.x]);
+        }
+    }
+    __shared__ int s_last;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int* ctr = p.ctr + (blockIdx.y * gridDim.z + blockIdx.z);
+        const int arrived = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = arrived == p.n_split - 1;
+        if (s_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    merge_group<T, D, kFoldSplits>(p, o_rs, b, g, rg, n_live, rows, grow0);
 }
 
-// Merge of the chunks: one wavefront per output row; lanes read the chunk
-// maxima and sums side by side, then accumulate the weighted partial outputs
-// with the head dimension across lanes, eight chunks' loads in flight at once.
+// Merge kernel (the fp32 kernel's chunks, and the 16-bit kernel's splits when
+// there are more than kFoldSplits): one wavefront per output row; lanes
+// read the chunk maxima and sums side by side, then accumulate the weighted
+// partial outputs with the head dimension across lanes, eight chunks' loads
+// in flight at once.
 struct MergeParams {
     const float* ws_o;
     const float* ws_m;
@@ -748,7 +913,9 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
         const int64_t n_rg = (int64_t(a.Hq / a.Hkv) * a.Sq + kDecRowsMfma - 1) / kDecRowsMfma;
         stream_splits(a.B * a.Hkv * n_rg, a.Sk, a.n_split, n_split, dp.split_keys);
     }
-    float* ws = static_cast<float*>(a.workspace);
+    // the workspace: arrival counters, then the partial results
+    dp.ctr = nullptr;
+    float* ws = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + attn_detail::kDecodeCounterBytes);
     dp.ws_o = ws;
     dp.ws_m = ws + int64_t(n_split) * rows * a.D;
     dp.ws_l = dp.ws_m + int64_t(n_split) * rows;
@@ -767,6 +934,11 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
     dp.causal = a.causal;
     if constexpr (sizeof(T) == 2) {
         const int n_rg = (dp.R + kDecRowsMfma - 1) / kDecRowsMfma;
+        // more than one split only when the groups number fewer than 256
+        // (stream_splits), so their counters fit the workspace's header
+        if (n_split > 1 && a.B * a.Hkv * n_rg * int64_t(sizeof(int)) > attn_detail::kDecodeCounterBytes)
+            return ATTN_ERR_LAUNCH;
+        if (n_split > 1 && n_split <= kFoldSplits) dp.ctr = static_cast<int*>(a.workspace);
         attn_detail::log_launch("decode_stream_kernel<%s, D=%d> grid=(%d, %lld, %d) block=%d split_keys=%d Sk=%lld "
                                 "Sq=%lld",
                                 attn_detail::dtype_name(a.dtype), D, n_split, (long long)(a.B * a.Hkv), n_rg,
@@ -782,8 +954,9 @@ int launch_decode_t(const attn_detail::DecodeArgs& a) {
                            dim3(kDecThreads), 0, static_cast<hipStream_t>(a.stream), dp);
     }
     hipError_t e = hipGetLastError();
-    // the streamed kernel with one split writes the output itself
-    if (e == hipSuccess && (sizeof(T) == 4 || n_split > 1)) {
+    // the streamed kernel writes the output itself with one split, or with
+    // up to kFoldSplits (its last split merges)
+    if (e == hipSuccess && (sizeof(T) == 4 || (n_split > 1 && dp.ctr == nullptr))) {
         MergeParams mp;
         mp.ws_o = dp.ws_o;
         mp.ws_m = dp.ws_m;
@@ -819,6 +992,8 @@ int launch_decode_dtype(const attn_detail::DecodeArgs& a) {
 // fixed device array, one copy per GPU for the life of the process.  In host
 // code the name below is a host-side stand-in, never a device address: the
 // device address is looked up with hipGetSymbolAddress, once per device.
+// Without an initialiser the array is zero when the code object is loaded
+// (static storage), which is what its leading arrival counters need.
 static __device__ __align__(256) float attn_decode_scratch[attn_detail::kDecodeScratchBytes / sizeof(float)];
 
 namespace attn_detail {

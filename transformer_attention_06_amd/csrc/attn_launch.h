@@ -142,6 +142,12 @@ int64_t decode_splits(int64_t Sk);
 // point (one array per GPU, shared by every call on that GPU).
 constexpr int64_t kDecodeScratchBytes = int64_t(32) << 20;
 
+// Every decode workspace starts with this many bytes of arrival counters
+// (one int per (batch, kv head, group of query rows) of a split launch; a
+// launch with more than one split has fewer than 256 such groups), zero
+// before a call and zero again after it; the partial results follow.
+constexpr int64_t kDecodeCounterBytes = 1024;
+
 // This device's address of that workspace (looked up on the first call on
 // each device); ATTN_OK or ATTN_ERR_DEVICE.
 int decode_scratch(void** ws);
