@@ -22,7 +22,10 @@ def _close(a, b, atol, what=""):
     b = np.asarray(b, dtype=np.float64)
     assert a.shape == b.shape, (what, a.shape, b.shape)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    err = np.where(both_inf, 0.0, np.abs(np.nan_to_num(a - b, nan=np.inf)))
+    # subtract only where the two are not the same infinity (inf - inf is NaN);
+    # any other NaN difference counts as an infinite error
+    d = np.subtract(a, b, out=np.zeros_like(a), where=~both_inf)
+    err = np.abs(np.nan_to_num(d, nan=np.inf))
     assert np.all(err <= atol), f"{what}: max err {err.max()} at {np.argwhere(err > atol)[:3]}"
 
 
