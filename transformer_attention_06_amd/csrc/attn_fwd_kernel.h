@@ -64,21 +64,26 @@ static_assert(BM == 4 * 32, "4 wavefronts x 32 rows");
 // SIMD.
 // Head dims above 160 (16-bit types) run one group with one wavefront per
 // SIMD: their output accumulators (8 blocks at D = 256) live in AGPRs
-// beside a full set of VGPRs.
+// beside a full set of VGPRs.  At D = 64 (16-bit, one-group workgroups,
+// no LSE, no mask tensor) a wavefront fits in 168 registers with operands
+// read four MFMAs ahead instead of six, so three workgroups share a CU
+// (three wavefronts per SIMD): at this head dim the softmax's VALU stream
+// outweighs the MFMAs, and a third wavefront fills more of its stalls.
 template <typename T, int D, bool CAUSAL>
 struct Groups {
     static constexpr int value = sizeof(T) == 2 && CAUSAL && D <= 160 ? 2 : 1;
 };
-template <typename T, int D>
+template <typename T, int D, bool CAUSAL, bool LSE, int MK>
 struct WavesPerSimd {
-    static constexpr int value = sizeof(T) == 2 && D > 160 ? 1 : 2;
+    static constexpr int value =
+        sizeof(T) == 2 && D > 160 ? 1 : (sizeof(T) == 2 && D == 64 && !CAUSAL && !LSE && MK == 0 ? 3 : 2);
 };
 
 // Work of one group: one (batch, query head, 128-row query block); four
 // wavefronts of 32 rows each.  Two groups share a CU (two wavefronts per
-// SIMD), so the stalls of one wavefront's stream are filled by the other's:
-// two one-group workgroups, or one workgroup of two groups pairing a causal
-// heavy and light block.
+// SIMD; three at D = 64, see WavesPerSimd), so the stalls of one
+// wavefront's stream are filled by the other's: one-group workgroups, or
+// one workgroup of two groups pairing a causal heavy and light block.
 //
 // Each wavefront software-pipelines its own tile loop.  Step j (key tile j)
 // is one fixed instruction stream of two parts:
@@ -98,7 +103,8 @@ struct WavesPerSimd {
 // step, waited on by that wavefront alone), and adds it to (or selects)
 // the scores of that tile before their row maxima are taken.
 template <typename T, int D, bool CAUSAL, bool PAD, bool LSE, bool ROPE, int MK = 0>
-__global__ __launch_bounds__(kThreads * (Groups<T, D, CAUSAL>::value), (WavesPerSimd<T, D>::value)) void attn_fwd_kernel(
+__global__ __launch_bounds__(kThreads * (Groups<T, D, CAUSAL>::value), (WavesPerSimd<T, D, CAUSAL, LSE, MK>::value))
+void attn_fwd_kernel(
     KParams p) {
     using E = Elem<T>;
     using op_t = typename E::op_t;
@@ -126,13 +132,14 @@ __global__ __launch_bounds__(kThreads * (Groups<T, D, CAUSAL>::value), (WavesPer
     constexpr int NDB = (D + 31) / 32;     // 32-dim blocks of O
     constexpr int NF = 16 * NBLK;          // scores per lane per tile
     constexpr int NG = Groups<T, D, CAUSAL>::value;  // wavefront groups
-    constexpr bool ACC_A = WavesPerSimd<T, D>::value == 1;  // output accumulators in AGPRs
+    constexpr int WPS = WavesPerSimd<T, D, CAUSAL, LSE, MK>::value;
+    constexpr bool ACC_A = WPS == 1;       // output accumulators in AGPRs
     constexpr int NBUF = 2;                // LDS buffers per operand and group
     constexpr int KD = NBUF == 4 ? 3 : 2;  // step t loads K tile t+KD
     constexpr int VD = NBUF == 4 ? 3 : 1;  // and V tile t+VD
     constexpr int N1 = NC * NBLK;          // Sᵀ MFMAs per tile
     constexpr int N2 = NKC * NDB;          // P·V MFMAs per tile
-    constexpr int PF = 6;                  // operand prefetch distance (MFMAs)
+    constexpr int PF = WPS == 3 ? 4 : 6;   // operand prefetch distance (MFMAs)
     static_assert(NBUF * TILE_E * ES <= 65536, "buffer offsets fit the LDS immediate");
 
     // Per group: K tiles [NBUF][BN][DL], then V tiles [NBUF][BN][DL], slots
