@@ -65,10 +65,11 @@ static_assert(BM == 4 * 32, "4 wavefronts x 32 rows");
 // Head dims above 160 (16-bit types) run one group with one wavefront per
 // SIMD: their output accumulators (8 blocks at D = 256) live in AGPRs
 // beside a full set of VGPRs.  At D = 64 (16-bit, one-group workgroups,
-// no LSE, no mask tensor) a wavefront fits in 168 registers with operands
-// read four MFMAs ahead instead of six, so three workgroups share a CU
-// (three wavefronts per SIMD): at this head dim the softmax's VALU stream
-// outweighs the MFMAs, and a third wavefront fills more of its stalls.
+// no LSE, no mask tensor) a wavefront fits in 168 registers, without
+// spills, with operands read three MFMAs ahead instead of six, so three
+// workgroups share a CU (three wavefronts per SIMD): at this head dim the
+// softmax's VALU stream outweighs the MFMAs, and a third wavefront fills
+// more of its stalls.
 template <typename T, int D, bool CAUSAL>
 struct Groups {
     static constexpr int value = sizeof(T) == 2 && CAUSAL && D <= 160 ? 2 : 1;
@@ -139,7 +140,7 @@ void attn_fwd_kernel(
     constexpr int VD = NBUF == 4 ? 3 : 1;  // and V tile t+VD
     constexpr int N1 = NC * NBLK;          // Sᵀ MFMAs per tile
     constexpr int N2 = NKC * NDB;          // P·V MFMAs per tile
-    constexpr int PF = WPS == 3 ? 4 : 6;   // operand prefetch distance (MFMAs)
+    constexpr int PF = WPS == 3 ? 3 : 6;   // operand prefetch distance (MFMAs)
     static_assert(NBUF * TILE_E * ES <= 65536, "buffer offsets fit the LDS immediate");
 
     // Per group: K tiles [NBUF][BN][DL], then V tiles [NBUF][BN][DL], slots
