@@ -198,9 +198,9 @@ void attn_fwd_kernel(
 
     // With two groups (causal masking only) a task is a pair of query blocks
     // of one (batch, query head): the heaviest and the lightest remaining
-    // block (qh = n_qb-1-task, ql = task).  Group 1 takes the light block and
-    // then the first nb key tiles of the heavy block, group 0 the rest of the
-    // heavy block; nb evens out the two groups' tile counts, and the heavy
+    // block (qh = n_qb-1-task, ql = task).  Group 0 takes the heavy block's
+    // key tiles up to its last nb, group 1 the light block and then those
+    // last nb tiles; nb evens out the two groups' tile counts, and the heavy
     // block's two partial softmax states are merged through LDS at the end.
     // With one group a task is one block; under causal masking heaviest
     // first for the first half of the launch and lightest first for the
@@ -237,9 +237,9 @@ void attn_fwd_kernel(
     const int Tl = tiles_of(ql);
     int nb = 0;
     // Both groups pass the same barriers, one per step, so the work is
-    // balanced by barrier count: group 0 passes Th - nb + 1, group 1 (light
-    // block, then the heavy block's first nb tiles, one barrier between)
-    // Tl + nb + 3.
+    // balanced by barrier count: group 0 (the heavy block's first Th - nb
+    // tiles) passes Th - nb + 1, group 1 (light block, then the heavy block's
+    // last nb tiles, one barrier between) Tl + nb + 3.
     if (NG == 2) nb = ql >= 0 ? (Th - Tl > 2 ? (Th - Tl - 2) / 2 : 0) : Th / 2;
 
     const int tid = threadIdx.x;
@@ -263,11 +263,15 @@ void attn_fwd_kernel(
         }
         ++nseg;
     };
+    // group 0 starts at the heavy block's first key tile, as group 1 starts
+    // at the light block's: every group of a head streams from tile 0 at the
+    // start of the launch, so the workgroups of a head read the same tiles at
+    // about the same time (L2 hits) instead of each from its own split point
     if (grp == 0) {
-        add_seg(qh, nb, Th, nb == 0);
+        add_seg(qh, 0, Th - nb, nb == 0);
     } else {
         if (ql >= 0) add_seg(ql, 0, Tl, true);
-        if (nb > 0) add_seg(qh, 0, nb, false);
+        if (nb > 0) add_seg(qh, Th - nb, Th, false);
     }
     // barriers a segment of n tiles passes (initial loads, Sᵀ of its first
     // tile, one per further tile); the groups pad to the same total
@@ -928,7 +932,7 @@ void attn_fwd_kernel(
     for (; n_bar < bars_all; ++n_bar) __syncthreads();
 
     // ---- merge the heavy block's two partial states ------------------------
-    // Group 1 leaves (m, l, O) of the heavy block's first nb tiles in LDS (the
+    // Group 1 leaves (m, l, O) of the heavy block's last nb tiles in LDS (the
     // tile buffers, idle now); group 0 combines them with its own:
     // m = max(m0, m1), O = O0·2^(m0-m) + O1·2^(m1-m), likewise the sums.
     if constexpr (NG == 2) {
