@@ -163,10 +163,17 @@ void attn_fwd_kernel(
     // ---- work decomposition ------------------------------------------------
     // Workgroup i runs on XCD i % 8.  Logical units (batch, kv head, query
     // head) are split into 8 contiguous ranges, one per XCD, so the query
-    // heads sharing a K/V head share that XCD's L2.
+    // heads sharing a K/V head share that XCD's L2.  Without causal masking
+    // the query blocks of a unit are dispatched one after another (task-minor
+    // order): they all stream the same K/V tiles from the first, at about the
+    // same time, so the tiles are read from memory once and shared in L2.
     const int wg = blockIdx.x;
     int unit, task;
-    if (p.xcd_chunk > 0) {
+    if (p.xcd_chunk > 0 && !CAUSAL) {
+        const int xcd = wg & 7, local = wg >> 3;
+        task = local % p.n_qb;
+        unit = xcd * p.xcd_chunk + local / p.n_qb;
+    } else if (p.xcd_chunk > 0) {
         const int xcd = wg & 7, local = wg >> 3;
         task = local / p.xcd_chunk;
         unit = xcd * p.xcd_chunk + local % p.xcd_chunk;
