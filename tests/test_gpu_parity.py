@@ -308,3 +308,25 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
         run(qd, kd, vd, causal=False)  # eager work between replays
+
+
+# --------------------------------------------------------------------------
+# work order: a multiple of 8 (batch, query head) units, so each XCD's range
+# of units is used; without causal masking a unit's query blocks run one
+# after another, under causal masking the pairs split the heavy block at
+# its last tiles, and an odd block count leaves an unpaired middle block
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,D,causal,padded", [
+    ("fp16", 64, False, True),    # three wavefronts per SIMD, task-minor order
+    ("bf16", 64, False, False),
+    ("bf16", 128, False, True),
+    ("bf16", 128, True, False),   # causal pairs, middle block alone
+    ("fp16", 64, True, True),
+    ("fp32", 64, False, False),
+])
+def test_work_order_shapes(dtype, D, causal, padded):
+    for (S, Hq, Hkv) in ((640, 8, 2), (384, 4, 4), (1152, 8, 8)):
+        print(f"work order case {dtype} D{D} S{S} H{Hq}/{Hkv} causal={causal} padded={padded}", flush=True)
+        o, l, ro, rl = _case(4242 + S + Hq, 2, S, Hq, Hkv, D, dtype, causal, padded)
+        assert_parity(o, ro, dtype, lse=l, lse_ref=rl,
+                      what=f"work order {dtype} D{D} S{S} H{Hq}/{Hkv} c{causal} p{padded}")
